@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+Prints one JSON line: tokens/s of the whole layer (moe_forward), the
+grouped-FFN phase's TFLOP/s against the bf16 dense matrix-core peak (measured
+live with HIP events on the stream the kernels run on), per-phase times and
+HBM rates, and the CPU oracle's throughput on the machine's host cores.
+
+A step is one forward of the whole layer (route, permute, grouped FFN,
+combine) over one batch of T tokens already resident in HBM.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/sec and grouped-FFN TFLOP/s as % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic_bytes(cfg):
+    """Bytes each phase must move at minimum (inputs read once, outputs written once)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k, de = cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert
+    R = T * k
+    return {
+        "route": T * d * es + d * E * es + R * 8,
+        "permute": R * 4 + T * d * es + R * 8 + R * d * es,
+        "ffn": R * d * es + 2 * E * d * de * es + 2 * R * de * es + R * d * es,
+        "combine": R * d * es + R * 8 + T * d * es,
+    }
+
+
+def ensure_built():
+    lib = os.path.join(ROOT, "sparse_mixture_experts_route_amd", "libmoe.so")
+    if not os.path.exists(lib):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "sparse_mixture_experts_route_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+
+
+def cpu_baseline(cfg, inp, sample_tokens):
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the same inputs."""
+    import numpy as np
+    import oracle
+    from harness import host_array
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    S = min(sample_tokens, cfg.T)
+    x = host_array(inp["x"][:S])
+    wr = host_array(inp["w_router"])
+    b = host_array(inp["router_bias"])
+    W1, W2 = host_array(inp["W1"]), host_array(inp["W2"])
+    t0 = time.perf_counter()
+    out = oracle.forward(x, wr, b, W1, W2, cfg.k, cfg.dtype)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["y"]).all()
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full expert weights; "
+                      f"{dt:.2f} s wall (NumPy float64, BLAS threads={threads}, host cpus={os.cpu_count()})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_coarse",
+                    help="workload: tiny_fp32, mixtral_coarse, fine_grained, skewed, large_sparse")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs the MoE layer on one GPU only; use --gpus 1 "
+              "(the multi-GPU expert-parallel layout is a design note, not an implementation)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    ensure_built()
+    import sparse_mixture_experts_route_amd as moe
+    from harness import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(cfg, seed=args.seed, device=dev)
+    x, wr, b, W1, W2 = inp["x"], inp["w_router"], inp["router_bias"], inp["W1"], inp["W2"]
+    layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, x.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- timed region A: whole-layer steps through moe_forward
+    for _ in range(args.warmup):
+        layer(x, wr, W1, W2, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        layer(x, wr, W1, W2, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- timed region B: the same work through the four stage entry points,
+    # with HIP events between phases on the stream the kernels run on
+    p = layer.problem
+    R = cfg.T * cfg.k
+    bufs = layer.stages(x, wr, W1, W2, b, logits=False)  # allocates the stage outputs once
+    ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
+    names = ["route", "permute", "ffn", "combine"]
+
+    def stage_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_route(p, x, wr, b, None, bufs["idx"], bufs["gate"])
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_permute(p, bufs["idx"], x, bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"],
+                        bufs["x_perm"], ws_p)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_grouped_ffn(p, bufs["x_perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.moe_combine(p, bufs["y_perm"], bufs["inv"], bufs["gate"], bufs["y"])
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        stage_step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        stage_step(events[s])
+    torch.cuda.synchronize()
+    phase_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, n in enumerate(names)}
+    assert torch.equal(bufs["y"], layer.y), "stage path and moe_forward disagree"
+
+    flops = cfg.ffn_flops()
+    bytes_ = algorithmic_bytes(cfg)
+    t_ffn = phase_ms["ffn"] * 1e-3
+    ffn_tflops = flops / t_ffn / 1e12
+    if cfg.dtype == "bf16":
+        roofline = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "grouped FFN phase: gemm_bf16_kernel x2 (GEMM1+GELU, GEMM2)"}
+    else:
+        gbs = bytes_["ffn"] / t_ffn / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
+                    "kernel": "grouped FFN phase: gemm_f32_kernel x2"}
+
+    phases = {n: {"ms": round(phase_ms[n], 4),
+                  "GB/s": round(bytes_[n] / (phase_ms[n] * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(bytes_[n] / (phase_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+              for n in names}
+    phases["ffn"]["TFLOP/s"] = round(ffn_tflops, 2)
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded normal inputs and random-init expert weights of the workload's shapes)",
+        "config": {**cfg.describe(), "parallelism": "none (1 GPU, all experts local)"},
+        "ffn_tflops": round(ffn_tflops, 2),
+        "ffn_frac_of_bf16_peak": round(ffn_tflops / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
+        "phases": phases,
+        "roofline": roofline,
+        "wall_s_timed_region": round(wall, 4),
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

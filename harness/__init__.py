@@ -7,4 +7,12 @@ tests and benchmark may use it without sharing any of the method's code.
 """
 
 from .configs import CONFIGS, MoEConfig, get_config, scaled_config  # noqa: F401
-from .inputs import make_inputs, to_host_arrays  # noqa: F401
+from .inputs import (  # noqa: F401
+    host_array,
+    make_dense,
+    make_exact_router_inputs,
+    make_group_offsets,
+    make_inputs,
+    make_routing_table,
+    to_host_arrays,
+)

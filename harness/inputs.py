@@ -17,7 +17,7 @@ arithmetic.
 
 from __future__ import annotations
 
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 import torch
@@ -56,12 +56,13 @@ def _normal(shape, std: float, seed: int, tensor: int, slice_: int, device, dtyp
 
 
 def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu",
-                router_zero: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+                router_zero: bool = False, weights: bool = True) -> Dict[str, Optional[torch.Tensor]]:
     """Draw x[T,d], w_router[d,E], router_bias[E] (or None), W1[E,d,de], W2[E,de,d].
 
     All tensors are contiguous, row-major, on `device`, in the workload dtype
     (the bias is float32). With `router_zero` the router weights and bias are
-    exact zeros (every logit is then exactly 0).
+    exact zeros (every logit is then exactly 0). With `weights=False` the expert
+    weights are not drawn (W1 and W2 are None).
     """
     dev = torch.device(device)
     dt = torch_dtype(cfg.dtype)
@@ -76,6 +77,8 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu",
         bias = torch.zeros(cfg.E, device=dev, dtype=torch.float32) if bv is not None else None
     elif bv is not None:
         bias = torch.tensor(bv, dtype=torch.float32, device=dev)
+    if not weights:
+        return {"x": x, "w_router": wr, "router_bias": bias, "W1": None, "W2": None}
     W1 = torch.empty((cfg.E, cfg.d_model, cfg.d_expert), device=dev, dtype=dt)
     W2 = torch.empty((cfg.E, cfg.d_expert, cfg.d_model), device=dev, dtype=dt)
     for e in range(cfg.E):
@@ -96,3 +99,83 @@ def host_array(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
 
 def to_host_arrays(inputs: Dict[str, Optional[torch.Tensor]]) -> Dict[str, Optional[np.ndarray]]:
     return {k: host_array(v) for k, v in inputs.items()}
+
+
+def make_exact_router_inputs(cfg: MoEConfig, seed: int = 0, device="cpu", bias: bool = False,
+                             tie_group: int = 1):
+    """Router inputs whose float32 logits are exact whatever the summation order.
+
+    x takes values in {-3..3}/4 and w_router in {-7..7}/64 (exact in bf16 and
+    float32), so every product is a multiple of 2^-8 and every partial sum of a
+    row stays below 2^15 in magnitude for d_model <= 2^14: all partial sums are
+    exactly representable. Equal logits are frequent, which exercises the
+    tie-break. With `bias`, a bias in multiples of 1/8 is added. With
+    tie_group = g > 1, experts come in runs of g identical router columns (and
+    biases), so every token has exact ties, also at the k-th place.
+    """
+    dev = torch.device(device)
+    dt = torch_dtype(cfg.dtype)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_mix(seed, 11, 0))
+    x = (torch.randint(-3, 4, (cfg.T, cfg.d_model), generator=g).float() / 4).to(dt).to(dev)
+    wr = (torch.randint(-7, 8, (cfg.d_model, cfg.E), generator=g).float() / 64).to(dt).to(dev)
+    b = None
+    if bias:
+        b = (torch.randint(-16, 17, (cfg.E,), generator=g).float() / 8).to(dev)
+    if tie_group > 1:
+        src = (torch.arange(cfg.E) // tie_group) * tie_group
+        wr = wr[:, src.to(dev)].contiguous()
+        if b is not None:
+            b = b[src.to(dev)].contiguous()
+    return {"x": x, "w_router": wr, "router_bias": b}
+
+
+def make_routing_table(T: int, E: int, k: int, seed: int = 0, device="cpu",
+                       hot: Optional[Tuple[int, ...]] = None, cold: Tuple[int, ...] = ()) -> torch.Tensor:
+    """A random routing table idx[T,k] int32: k distinct experts per token.
+
+    `hot` experts are chosen by every token (when k allows); `cold` experts are
+    never chosen, which leaves their groups empty.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_mix(seed, 12, T * 1000003 + E * 131 + k))
+    allowed = [e for e in range(E) if e not in set(cold)]
+    hot = tuple(e for e in (hot or ()) if e in allowed)[:k]
+    rest = [e for e in allowed if e not in hot]
+    need = k - len(hot)
+    if need > len(rest):
+        raise ValueError("not enough experts left for k distinct choices")
+    scores = torch.rand((T, len(rest)), generator=g)
+    pick = torch.argsort(scores, dim=1)[:, :need]
+    rest_t = torch.tensor(rest, dtype=torch.int64)
+    cols = [torch.full((T, 1), h, dtype=torch.int64) for h in hot] + [rest_t[pick]]
+    idx = torch.cat(cols, dim=1)
+    # shuffle the order inside each row so hot experts are not always first
+    order = torch.argsort(torch.rand((T, k), generator=g), dim=1)
+    idx = torch.gather(idx, 1, order)
+    return idx.to(torch.int32).to(device)
+
+
+def make_group_offsets(E: int, rows: int, seed: int = 0, empty: Tuple[int, ...] = ()) -> torch.Tensor:
+    """offsets[E+1] (int32, on the CPU) of random ragged group sizes summing to `rows`.
+
+    Experts listed in `empty` get no rows.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_mix(seed, 13, E * 7919 + rows))
+    live = [e for e in range(E) if e not in set(empty)]
+    if not live:
+        raise ValueError("at least one non-empty group is needed")
+    w = torch.rand(len(live), generator=g) + 0.05
+    sizes = torch.floor(w / w.sum() * rows).to(torch.int64)
+    sizes[0] += rows - int(sizes.sum())
+    counts = torch.zeros(E, dtype=torch.int64)
+    counts[torch.tensor(live)] = sizes
+    off = torch.zeros(E + 1, dtype=torch.int64)
+    off[1:] = torch.cumsum(counts, 0)
+    return off.to(torch.int32)
+
+
+def make_dense(shape, std: float, seed: int, tag: int, device="cpu", dtype: str = "bf16") -> torch.Tensor:
+    """A seeded normal tensor in the workload dtype (for stage-level parity inputs)."""
+    return _normal(tuple(shape), std, seed, 20 + tag, 0, torch.device(device), torch_dtype(dtype))

@@ -1,0 +1,145 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer (from "Distributed training part 4", jesamkim's AI tech blog,
+ * section 3 "Mixture of Experts" and section 4 "Expert Parallelism"):
+ *   router: a Linear layer followed by a Softmax over the E experts;
+ *   selection: the k experts with the largest router output per token;
+ *   dispatch: each token goes to the experts it selected;
+ *   experts: E independent FFNs, E_i(x) = GELU_tanh(x W1_i) W2_i (no biases);
+ *   combine: y = sum over the selected i of G(x)_i * E_i(x), where G(x)_i is
+ *            the router probability of expert i.
+ * All experts live on one GPU, so dispatch and combine are a local permutation
+ * (rows grouped by expert) and its inverse gather.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous buffers,
+ *     16-byte aligned. `p` is a HOST pointer, read during the call only.
+ *   - Ownership: the caller owns every buffer and the workspace. The library
+ *     allocates no device memory, keeps no pointer after returning, never
+ *     writes its inputs and fully overwrites its outputs (no accumulation).
+ *   - Asynchrony: each call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL is the null stream) and returns; it never synchronizes and never
+ *     copies device data to the host. Results are ready once the stream
+ *     reaches that point. Calls on different streams that share no output or
+ *     workspace buffer may run concurrently: the library has no global
+ *     mutable state.
+ *   - Errors: all argument checks run on the host before anything is
+ *     enqueued; on any error nothing is written. A failed kernel launch
+ *     returns MOE_ERR_HIP. Faults during execution show at the caller's next
+ *     synchronization. No C++ exception crosses this interface.
+ *   - Contract: T >= 1; 1 <= k <= E <= 256; T*k <= INT32_MAX; d_model and
+ *     d_expert are multiples of 64. The dtype of x, w_router, W1, W2, x_perm,
+ *     y_perm and y is p->dtype. Logits, gates and the router bias are float32;
+ *     indices, counts and offsets are int32. Inputs must be finite.
+ *   - Routing rule: selection is made on the float32 logits, in descending
+ *     order, ties going to the lower expert index; gates are the softmax over
+ *     all E logits (not renormalised over the k selected).
+ */
+#ifndef MOE_MI355X_MOE_H_
+#define MOE_MI355X_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,  /* NULL pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,       /* legal in principle but outside this build's contract */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Which entry point a workspace size is asked for. */
+typedef enum {
+  MOE_STAGE_PERMUTE = 0,
+  MOE_STAGE_GROUPED_FFN = 1,
+  MOE_STAGE_FORWARD = 2
+} moe_stage_t;
+
+typedef struct {
+  int64_t T;        /* tokens */
+  int32_t d_model;  /* hidden size */
+  int32_t E;        /* experts */
+  int32_t k;        /* experts selected per token */
+  int32_t d_expert; /* expert FFN width (G = d_ff / d_expert in the MOSAIC summary) */
+  int32_t dtype;    /* a moe_dtype_t */
+} moe_problem_t;
+
+/* Workspace bytes that `stage` needs for problem `p` (host only, no HIP call).
+ * moe_route and moe_combine need none. */
+moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes);
+
+/* Router Linear + Softmax + top-k (blog section 3, structure: the gating
+ * network is a Linear layer and a Softmax; only the top-k experts are used).
+ *   x            [T, d_model]      input tokens
+ *   w_router     [d_model, E]      router weight (logit = x w_router + bias)
+ *   router_bias  [E] float32 or NULL
+ *   logits       [T, E] float32 or NULL: the float32 logits the selection used
+ *   topk_idx     [T, k] int32: selected experts, descending logit, ties to the lower index
+ *   topk_gate    [T, k] float32: softmax probability of each selected expert */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                       const float* router_bias, float* logits, int32_t* topk_idx,
+                       float* topk_gate, void* stream);
+
+/* Dispatch as a local permutation (blog section 4, dispatch: each token is
+ * sent to the expert it chose). Rows are grouped by expert; inside a group
+ * tokens keep their order.
+ *   topk_idx [T, k] int32 in [0, E), distinct within a token (entries outside
+ *            [0, E) are ignored; duplicates give unspecified but in-bounds output)
+ *   x        [T, d_model]
+ *   counts   [E]     int32: selections per expert
+ *   offsets  [E + 1] int32: exclusive prefix sum of counts, offsets[E] = T*k
+ *   perm     [T*k]   int32: token of each permuted row
+ *   inv      [T*k]   int32: inv[t*k + j] = row of selection (t, j) (-1 if ignored)
+ *   x_perm   [T*k, d_model]: x_perm[r] = x[perm[r]]
+ *   ws       workspace of at least moe_workspace_size(p, MOE_STAGE_PERMUTE) bytes */
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                         void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* The expert FFNs over their row groups as two grouped GEMMs (blog section 3:
+ * independent FFN experts; the MOSAIC summary's performance model counts them
+ * as grouped GEMMs). For every expert e and row r in [offsets[e], offsets[e+1]):
+ *   y_perm[r] = GELU_tanh(x_perm[r] W1[e]) W2[e]
+ * with float32 accumulation; the hidden activation is stored in p->dtype.
+ *   x_perm  [T*k, d_model]
+ *   offsets [E + 1] int32, non-decreasing, offsets[0] = 0, offsets[E] <= T*k
+ *   W1      [E, d_model, d_expert]
+ *   W2      [E, d_expert, d_model]
+ *   y_perm  [T*k, d_model]: rows outside [0, offsets[E]) are left untouched
+ *   ws      at least moe_workspace_size(p, MOE_STAGE_GROUPED_FFN) bytes */
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
+                             const void* W1, const void* W2, void* y_perm,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (blog section 3 output formula; section 4, combine:
+ * expert results return to their token):
+ *   y[t] = sum over j < k of topk_gate[t, j] * y_perm[inv[t*k + j]]
+ * accumulated in float32 in selection order; entries of inv outside
+ * [0, T*k) contribute nothing.
+ *   y_perm [T*k, d_model], inv [T*k] int32, topk_gate [T, k] float32, y [T, d_model] */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* inv,
+                         const float* topk_gate, void* y, void* stream);
+
+/* The whole layer: route, permute, grouped FFN, combine on one stream, with
+ * every intermediate in the workspace.
+ *   ws at least moe_workspace_size(p, MOE_STAGE_FORWARD) bytes */
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
+                         const float* router_bias, const void* W1, const void* W2, void* y,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_MOE_H_ */

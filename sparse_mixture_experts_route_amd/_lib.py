@@ -1,0 +1,135 @@
+"""ctypes declarations of libmoe.so and argument marshalling for its entry points."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loaded first: libmoe.so then binds to the HIP runtime torch already mapped
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILE = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_STAGE_PERMUTE = 0
+MOE_STAGE_GROUPED_FFN = 1
+MOE_STAGE_FORWARD = 2
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_str(status)} (status {status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_expert", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_FILE):
+        raise ImportError(f"{_LIB_FILE} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_FILE, mode=ctypes.RTLD_GLOBAL)
+    P = ctypes.POINTER(Problem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sigs = {
+        "moe_workspace_size": [P, i32, ctypes.POINTER(sz)],
+        "moe_route": [P, vp, vp, vp, vp, vp, vp, vp],
+        "moe_permute": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_grouped_ffn": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_combine": [P, vp, vp, vp, vp, vp],
+        "moe_forward": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int32
+    lib.moe_status_str.argtypes = [i32]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib_path() -> str:
+    return _LIB_FILE
+
+
+def moe_status_str(status: int) -> str:
+    return _lib.moe_status_str(int(status)).decode()
+
+
+def make_problem(T: int, d_model: int, E: int, k: int, d_expert: int, dtype) -> Problem:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}[dtype]
+    elif isinstance(dtype, str):
+        dtype = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}[dtype]
+    return Problem(int(T), int(d_model), int(E), int(k), int(d_expert), int(dtype))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    """Device address of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def moe_workspace_size(p: Problem, stage: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.moe_workspace_size(ctypes.byref(p), int(stage), ctypes.byref(out)), "moe_workspace_size")
+    return int(out.value)
+
+
+def moe_route(p: Problem, x, w_router, router_bias, logits, topk_idx, topk_gate, stream=None):
+    _check(_lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(logits),
+                          _ptr(topk_idx), _ptr(topk_gate), _stream(stream)), "moe_route")
+
+
+def moe_permute(p: Problem, topk_idx, x, counts, offsets, perm, inv, x_perm, ws, stream=None):
+    _check(_lib.moe_permute(ctypes.byref(p), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(perm),
+                            _ptr(inv), _ptr(x_perm), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "moe_permute")
+
+
+def moe_grouped_ffn(p: Problem, x_perm, offsets, W1, W2, y_perm, ws, stream=None):
+    _check(_lib.moe_grouped_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(W2), _ptr(y_perm),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_combine(p: Problem, y_perm, inv, topk_gate, y, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(inv), _ptr(topk_gate), _ptr(y),
+                            _stream(stream)), "moe_combine")
+
+
+def moe_forward(p: Problem, x, w_router, router_bias, W1, W2, y, ws, stream=None):
+    _check(_lib.moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(W1), _ptr(W2),
+                            _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def raw_lib():
+    """The ctypes handle itself (for callers that pass raw addresses)."""
+    return _lib

@@ -1,0 +1,90 @@
+// Weighted combine: y[t] = sum over j < k of gate[t, j] * y_perm[inv[t*k + j]].
+//
+// "Distributed training part 4" (jesamkim's AI tech blog), section 3: the layer
+// output is the sum over the selected experts of the router weight times the
+// expert output; section 4, combine: the expert results return to the token
+// they came from. Gather form: one wave per token reads its k expert rows and
+// writes its own output row, so no atomics are needed and the result is
+// deterministic. Accumulation is float32, in selection order.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCombineWaves = 4;
+
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+    f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+  }
+}
+
+__global__ __launch_bounds__(kCombineWaves * kWave) void combine_bf16_kernel(
+    const u32x4* __restrict__ y_perm, const int32_t* __restrict__ inv, const float* __restrict__ gate,
+    u32x4* __restrict__ y, int64_t T, int k, int64_t row_vecs, int64_t rows) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kCombineWaves + threadIdx.x / kWave;
+  if (t >= T) return;
+  for (int64_t c = lane; c < row_vecs; c += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = inv[t * k + j];
+      if (r < 0 || r >= rows) continue;
+      const float g = gate[t * k + j];
+      float v[8];
+      unpack8(y_perm[(int64_t)r * row_vecs + c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    y[t * row_vecs + c] = o;
+  }
+}
+
+__global__ __launch_bounds__(kCombineWaves * kWave) void combine_f32_kernel(
+    const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv, const float* __restrict__ gate,
+    f32x4* __restrict__ y, int64_t T, int k, int64_t row_vecs, int64_t rows) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kCombineWaves + threadIdx.x / kWave;
+  if (t >= T) return;
+  for (int64_t c = lane; c < row_vecs; c += kWave) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = inv[t * k + j];
+      if (r < 0 || r >= rows) continue;
+      const float g = gate[t * k + j];
+      const f32x4 v = y_perm[(int64_t)r * row_vecs + c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    y[t * row_vecs + c] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv, const float* gate,
+                          void* y, hipStream_t s) {
+  const int64_t blocks = ceil_div(p.T, kCombineWaves);
+  const int64_t rows = p.T * p.k;
+  if (p.dtype == MOE_DTYPE_BF16) {
+    const int64_t row_vecs = p.d_model / 8;
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3((unsigned)blocks), dim3(kCombineWaves * kWave), 0, s,
+                       (const u32x4*)y_perm, inv, gate, (u32x4*)y, p.T, p.k, row_vecs, rows);
+  } else {
+    const int64_t row_vecs = p.d_model / 4;
+    hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)blocks), dim3(kCombineWaves * kWave), 0, s,
+                       (const f32x4*)y_perm, inv, gate, (f32x4*)y, p.T, p.k, row_vecs, rows);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef uint16_t bf16_bits;  // raw bfloat16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bfloat16, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// tanh-form GELU: u/2 * (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+// tanh z = 1 - 2 / (exp(2z) + 1), which saturates correctly at both ends.
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float z = c * (u + 0.044715f * u * u * u);
+  float t = 1.0f - 2.0f / (__expf(2.0f * z) + 1.0f);
+  return 0.5f * u * (1.0f + t);
+}
+
+// Order-preserving map of a float32 to uint32 (larger float -> larger key);
+// -0.0 is folded onto +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe

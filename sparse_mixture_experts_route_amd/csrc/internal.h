@@ -1,0 +1,37 @@
+// Internal launchers of the MoE layer kernels (host side). Each enqueues on
+// `s` and returns the launch status; arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kPermuteTokensPerBlock = 256;
+
+inline int64_t permute_blocks(int64_t T) { return (T + kPermuteTokensPerBlock - 1) / kPermuteTokensPerBlock; }
+
+hipError_t launch_route(const moe_problem_t& p, const void* x, const void* w_router, const float* bias,
+                        float* logits, int32_t* idx, float* gate, hipStream_t s);
+
+// counts/offsets/perm/inv from the routing table; blockcounts/blockbase are
+// workspace arrays of permute_blocks(T) * E int32 each.
+hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv,
+                                int32_t* blockcounts, int32_t* blockbase, hipStream_t s);
+
+// x_perm[inv[t*k+j]] = x[t] for every valid selection.
+hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* inv, void* x_perm,
+                         hipStream_t s);
+
+// C[r] = act(A[r] B[e]) for rows r of every expert group e (offsets[E+1]).
+// A [R, K], B [E, K, N], C [R, N]; act = GELU_tanh or identity.
+hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
+                               int64_t R, int K, int N, int E, bool gelu, hipStream_t s);
+
+hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv,
+                          const float* gate, void* y, hipStream_t s);
+
+}  // namespace moe

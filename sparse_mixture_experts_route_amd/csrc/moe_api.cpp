@@ -1,0 +1,220 @@
+// C ABI of the MoE layer forward: argument checks, workspace layout and
+// launch order. Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+inline size_t elem_size(int32_t dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->T < 1 || p->E < 1 || p->k < 1 || p->k > p->E || p->d_model < 1 || p->d_expert < 1)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (p->E > 256) return MOE_ERR_UNSUPPORTED;
+  if (p->T > (int64_t)INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
+  if (p->d_model % 64 != 0 || p->d_expert % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Sequential sub-allocation of a caller-provided workspace (or size counting when base is null).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t n) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* ptr = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return ptr;
+  }
+};
+
+struct PermuteWs {
+  int32_t* blockcounts;
+  int32_t* blockbase;
+};
+
+PermuteWs carve_permute(Carver& c, const moe_problem_t& p) {
+  const size_t n = (size_t)moe::permute_blocks(p.T) * (size_t)p.E;
+  PermuteWs w;
+  w.blockcounts = c.take<int32_t>(n);
+  w.blockbase = c.take<int32_t>(n);
+  return w;
+}
+
+void* carve_ffn(Carver& c, const moe_problem_t& p) {
+  return c.take<char>((size_t)p.T * p.k * p.d_expert * elem_size(p.dtype));
+}
+
+struct ForwardWs {
+  int32_t *idx, *counts, *offsets, *perm, *inv;
+  float* gate;
+  PermuteWs pw;
+  void *x_perm, *h, *y_perm;
+};
+
+ForwardWs carve_forward(Carver& c, const moe_problem_t& p) {
+  const size_t R = (size_t)p.T * p.k;
+  const size_t es = elem_size(p.dtype);
+  ForwardWs w;
+  w.idx = c.take<int32_t>(R);
+  w.gate = c.take<float>(R);
+  w.counts = c.take<int32_t>(p.E);
+  w.offsets = c.take<int32_t>(p.E + 1);
+  w.perm = c.take<int32_t>(R);
+  w.inv = c.take<int32_t>(R);
+  w.pw = carve_permute(c, p);
+  w.x_perm = c.take<char>(R * p.d_model * es);
+  w.h = carve_ffn(c, p);
+  w.y_perm = c.take<char>(R * p.d_model * es);
+  return w;
+}
+
+size_t stage_bytes(const moe_problem_t& p, int32_t stage) {
+  Carver c(nullptr);
+  switch (stage) {
+    case MOE_STAGE_PERMUTE:
+      carve_permute(c, p);
+      break;
+    case MOE_STAGE_GROUPED_FFN:
+      carve_ffn(c, p);
+      break;
+    default:
+      carve_forward(c, p);
+      break;
+  }
+  return c.off + kAlign;  // slack so a 16-byte aligned base can be rounded up to kAlign
+}
+
+inline char* align_ws(void* ws) { return (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign); }
+
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage != MOE_STAGE_PERMUTE && stage != MOE_STAGE_GROUPED_FFN && stage != MOE_STAGE_FORWARD)
+    return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = stage_bytes(*p, stage);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                               const float* router_bias, float* logits, int32_t* topk_idx, float* topk_gate,
+                               void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
+      (router_bias && !aligned16(router_bias)) || (logits && !aligned16(logits)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_route(*p, x, w_router, router_bias, logits, topk_idx, topk_gate,
+                                      (hipStream_t)stream));
+}
+
+MOE_API moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, const void* x, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !x_perm || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(topk_idx) || !aligned16(x) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) ||
+      !aligned16(inv) || !aligned16(x_perm) || !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_PERMUTE)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const PermuteWs w = carve_permute(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = moe::launch_permute_index(*p, topk_idx, counts, offsets, perm, inv, w.blockcounts, w.blockbase, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_gather(*p, x, inv, x_perm, s));
+}
+
+MOE_API moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
+                                     const void* W1, const void* W2, void* y_perm, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !offsets || !W1 || !W2 || !y_perm || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x_perm) || !aligned16(offsets) || !aligned16(W1) || !aligned16(W2) || !aligned16(y_perm) ||
+      !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_GROUPED_FFN)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  void* h = carve_ffn(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = p->T * p->k;
+  hipError_t e = moe::launch_grouped_gemm(p->dtype, x_perm, offsets, W1, h, R, p->d_model, p->d_expert, p->E,
+                                          true, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(
+      moe::launch_grouped_gemm(p->dtype, h, offsets, W2, y_perm, R, p->d_expert, p->d_model, p->E, false, s));
+}
+
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* inv,
+                                 const float* topk_gate, void* y, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !inv || !topk_gate || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_perm) || !aligned16(inv) || !aligned16(topk_gate) || !aligned16(y))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_combine(*p, y_perm, inv, topk_gate, y, (hipStream_t)stream));
+}
+
+MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
+                                 const float* router_bias, const void* W1, const void* W2, void* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !W1 || !W2 || !y || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(W1) || !aligned16(W2) || !aligned16(y) ||
+      !aligned16(ws) || (router_bias && !aligned16(router_bias)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_FORWARD)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const ForwardWs w = carve_forward(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = p->T * p->k;
+  hipError_t e = moe::launch_route(*p, x, w_router, router_bias, nullptr, w.idx, w.gate, s);
+  if (e == hipSuccess)
+    e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts, w.pw.blockbase, s);
+  if (e == hipSuccess) e = moe::launch_gather(*p, x, w.inv, w.x_perm, s);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.h, R, p->d_model, p->d_expert, p->E, true, s);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, w.h, w.offsets, W2, w.y_perm, R, p->d_expert, p->d_model, p->E, false,
+                                 s);
+  if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
+  return hip_status(e);
+}
+
+MOE_API const char* moe_status_str(int32_t status) {
+  switch (status) {
+    case MOE_OK:
+      return "ok";
+    case MOE_ERR_INVALID_ARGUMENT:
+      return "invalid argument";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported problem (outside the library's contract)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL:
+      return "workspace too small";
+    case MOE_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}

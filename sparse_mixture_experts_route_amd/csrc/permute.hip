@@ -1,0 +1,159 @@
+// Dispatch as a local permutation.
+//
+// "Distributed training part 4" (jesamkim's AI tech blog), section 4,
+// dispatch: every token is sent to the expert it selected. With all experts
+// on one GPU the exchange becomes a reordering of the T*k selections into
+// contiguous per-expert row groups, which the grouped GEMMs then read.
+//
+// The reordering is a stable counting sort, deterministic by construction:
+//   hist    per block of 256 tokens, a bit mask mask[e] marks the tokens that
+//           selected expert e (LDS atomicOr: the result does not depend on
+//           the order of the atomics); counts per (block, expert) = popcounts.
+//   scan    one workgroup: counts[e] over blocks, offsets[] as the exclusive
+//           prefix sum over experts, and the first row of every (block, expert).
+//   scatter the row of selection (t, j) is the base of (block, e) plus the
+//           number of tokens before t in the block that selected e (popcount
+//           of the mask below t), so rows follow token order inside a group.
+//   gather  token-major: each x row is read once and written to its k rows.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTB = kPermuteTokensPerBlock;  // tokens per block, one thread each
+constexpr int kWords = kTB / 32;             // mask words per expert
+
+__device__ __forceinline__ void build_mask(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                           uint32_t (*mask)[kWords], int64_t t0) {
+  uint32_t* flat = &mask[0][0];
+  for (int i = threadIdx.x; i < E * kWords; i += kTB) flat[i] = 0u;
+  __syncthreads();
+  const int64_t t = t0 + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr(&mask[e][threadIdx.x >> 5], 1u << (threadIdx.x & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTB) void hist_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                   int32_t* __restrict__ blockcounts) {
+  __shared__ uint32_t mask[256][kWords];
+  build_mask(idx, T, k, E, mask, (int64_t)blockIdx.x * kTB);
+  const int e = threadIdx.x;
+  if (e < E) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popc(mask[e][w]);
+    blockcounts[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// One workgroup of 256 threads, thread e owns expert e.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blockcounts, int64_t nb, int E,
+                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ blockbase) {
+  __shared__ int32_t s[256];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E)
+    for (int64_t b = 0; b < nb; ++b) total += blockcounts[b * E + e];
+  s[e] = total;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 256 slots
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t v = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  const int32_t excl = s[e] - total;
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = s[e];
+    int32_t run = excl;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int32_t c = blockcounts[b * E + e];
+      blockbase[b * E + e] = run;
+      run += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                      const int32_t* __restrict__ blockbase,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ uint32_t mask[256][kWords];
+  const int64_t t0 = (int64_t)blockIdx.x * kTB;
+  build_mask(idx, T, k, E, mask, t0);
+  const int64_t t = t0 + threadIdx.x;
+  if (t >= T) return;
+  const int w = threadIdx.x >> 5;
+  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    int32_t r = -1;
+    if ((unsigned)e < (unsigned)E) {
+      int rank = __popc(mask[e][w] & below);
+      for (int w2 = 0; w2 < w; ++w2) rank += __popc(mask[e][w2]);
+      r = blockbase[(int64_t)blockIdx.x * E + e] + rank;
+      perm[r] = (int32_t)t;
+    }
+    inv[t * k + j] = r;
+  }
+}
+
+// One wave per token: the row is read once in 16-byte pieces and written to
+// each of the token's k rows.
+constexpr int kGatherWaves = 4;
+
+__global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(const u32x4* __restrict__ x,
+                                                                      const int32_t* __restrict__ inv,
+                                                                      u32x4* __restrict__ x_perm, int64_t T,
+                                                                      int k, int64_t row_vecs, int64_t rows) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave;
+  if (t >= T) return;
+  const u32x4* src = x + t * row_vecs;
+  for (int64_t c = lane; c < row_vecs; c += kWave) {
+    const u32x4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = inv[t * k + j];
+      if (r >= 0 && r < rows) x_perm[(int64_t)r * row_vecs + c] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* blockcounts, int32_t* blockbase,
+                                hipStream_t s) {
+  const int64_t nb = permute_blocks(p.T);
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blockcounts, nb, p.E, counts, offsets, blockbase);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockbase, perm,
+                     inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* inv, void* x_perm,
+                         hipStream_t s) {
+  const int es = p.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_vecs = (int64_t)p.d_model * es / 16;
+  const int64_t blocks = ceil_div(p.T, kGatherWaves);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(kGatherWaves * kWave), 0, s, (const u32x4*)x,
+                     inv, (u32x4*)x_perm, p.T, p.k, row_vecs, p.T * p.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

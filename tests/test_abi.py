@@ -1,0 +1,123 @@
+"""The C ABI library on the host: it loads, exports what include/moe.h declares,
+sizes workspaces, and rejects bad arguments before anything reaches the GPU.
+
+No call here launches a kernel: every call fails argument validation on the
+host (or only computes a workspace size), so these tests need no GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
+        "moe_forward", "moe_status_str"])
+
+
+def test_library_exports_every_declared_symbol(libmoe_path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", libmoe_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # nothing else of the library leaks into the dynamic symbol table under the moe_ prefix
+    assert exported == set(declared_functions())
+
+
+@pytest.fixture(scope="module")
+def lib(moe):
+    from sparse_mixture_experts_route_amd import _lib
+    return _lib.raw_lib()
+
+
+def P(moe, T=64, d=128, E=8, k=2, de=256, dtype=1):
+    return moe.Problem(T, d, E, k, de, dtype)
+
+
+A = ctypes.c_void_p(0x10000)      # 16-byte aligned fake address (never dereferenced)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)    # misaligned
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_str(s)
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+def test_problem_validation(moe, lib):
+    bytes_ = ctypes.c_size_t(0)
+    cases = [
+        (P(moe), OK),
+        (P(moe, T=0), INVALID), (P(moe, k=0), INVALID), (P(moe, k=9), INVALID),
+        (P(moe, E=0), INVALID), (P(moe, dtype=7), INVALID), (P(moe, d=-64), INVALID),
+        (P(moe, E=257, k=2), UNSUPPORTED), (P(moe, d=96), UNSUPPORTED), (P(moe, de=32), UNSUPPORTED),
+        (P(moe, T=2 ** 30, k=2), UNSUPPORTED), (P(moe, T=2 ** 30 - 1, k=2), OK),
+        (P(moe, E=256, k=256), OK), (P(moe, E=1, k=1), OK),
+    ]
+    for p, want in cases:
+        assert lib.moe_workspace_size(ctypes.byref(p), 2, ctypes.byref(bytes_)) == want, (p.T, p.E, p.k)
+    assert lib.moe_workspace_size(None, 2, ctypes.byref(bytes_)) == INVALID
+    assert lib.moe_workspace_size(ctypes.byref(P(moe)), 9, ctypes.byref(bytes_)) == INVALID
+    assert lib.moe_workspace_size(ctypes.byref(P(moe)), 2, None) == INVALID
+
+
+def test_workspace_sizes_cover_the_intermediates(moe):
+    T, d, E, k, de = 4096, 2048, 8, 2, 8192
+    p = P(moe, T, d, E, k, de, 1)
+    R = T * k
+    ffn = moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN)
+    fwd = moe.moe_workspace_size(p, moe.MOE_STAGE_FORWARD)
+    per = moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE)
+    assert ffn >= R * de * 2
+    assert fwd >= R * (2 * d + de) * 2 + 4 * R * 4 + ffn - R * de * 2
+    assert per >= 2 * ((T + 255) // 256) * E * 4
+    assert fwd < R * (2 * d + de) * 2 + 64 * 2 ** 20  # no hidden extra buffers
+
+
+def test_route_rejects_before_launch(moe, lib):
+    p = P(moe)
+    s = ctypes.c_void_p(0)
+    assert lib.moe_route(ctypes.byref(p), None, A, None, None, A, A, s) == INVALID
+    assert lib.moe_route(ctypes.byref(p), A, A, None, None, None, A, s) == INVALID
+    assert lib.moe_route(ctypes.byref(p), MIS, A, None, None, A, A, s) == INVALID
+    assert lib.moe_route(ctypes.byref(p), A, A, MIS, None, A, A, s) == INVALID
+    assert lib.moe_route(ctypes.byref(P(moe, k=0)), A, A, None, None, A, A, s) == INVALID
+    assert lib.moe_route(ctypes.byref(P(moe, d=100)), A, A, None, None, A, A, s) == UNSUPPORTED
+
+
+def test_permute_ffn_forward_reject_small_workspace(moe, lib):
+    p = P(moe)
+    s = ctypes.c_void_p(0)
+    need_p = moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE)
+    need_f = moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN)
+    need_w = moe.moe_workspace_size(p, moe.MOE_STAGE_FORWARD)
+    assert lib.moe_permute(ctypes.byref(p), A, A, A, A, A, A, A, A2, need_p - 1, s) == WS_SMALL
+    assert lib.moe_grouped_ffn(ctypes.byref(p), A, A, A, A, A, A2, need_f - 1, s) == WS_SMALL
+    assert lib.moe_forward(ctypes.byref(p), A, A, None, A, A, A, A2, need_w - 1, s) == WS_SMALL
+    assert lib.moe_permute(ctypes.byref(p), A, A, A, A, A, A, A, None, need_p, s) == INVALID
+    assert lib.moe_grouped_ffn(ctypes.byref(p), A, MIS, A, A, A, A2, need_f, s) == INVALID
+    assert lib.moe_forward(ctypes.byref(p), A, A, MIS, A, A, A, A2, need_w, s) == INVALID
+    assert lib.moe_combine(ctypes.byref(p), A, A, None, A, s) == INVALID
+    assert lib.moe_combine(ctypes.byref(P(moe, E=300)), A, A, A, A, s) == UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors(moe):
+    import torch
+    p = moe.make_problem(64, 128, 8, 2, 256, torch.float32)
+    x = torch.zeros(64, 128)
+    with pytest.raises(ValueError):
+        moe.moe_route(p, x, x, None, None, x, x)

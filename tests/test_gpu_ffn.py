@@ -1,0 +1,91 @@
+"""moe_grouped_ffn on the GPU against the oracle's per-expert FFN on the same
+permuted rows and group offsets (ragged, with empty groups and tile tails)."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL_BF16, TOL_F32, announce, f64, needs_gpu, rel_err
+from harness import host_array, make_dense, make_group_offsets
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def run_ffn(moe, R, d, de, E, dtype, x_perm, offsets, W1, W2):
+    # the problem's T*k must cover the rows; use k = 1, T = R
+    p = moe.make_problem(R, d, E, 1, de, dtype)
+    y = torch.full((R, d), float("nan"), dtype=x_perm.dtype, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_ffn(p, x_perm, offsets, W1, W2, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_ffn(dtype, x_perm, offsets, W1, W2):
+    xp = oracle.decode(host_array(x_perm), dtype)
+    w1, w2 = host_array(W1), host_array(W2)
+    return oracle.grouped_ffn(xp, host_array(offsets), lambda e: oracle.decode(w1[e], dtype),
+                              lambda e: oracle.decode(w2[e], dtype))
+
+
+CASES = [
+    # R, d, de, E, dtype, empty groups
+    (1, 64, 64, 1, "bf16", ()),
+    (100, 128, 256, 8, "f32", ()),
+    (777, 256, 192, 5, "f32", (2,)),
+    (300, 128, 256, 8, "bf16", ()),
+    (1000, 256, 512, 8, "bf16", (3, 4)),
+    (2500, 512, 384, 16, "bf16", (0, 15)),
+    (4096, 1024, 1024, 4, "bf16", ()),
+    (1537, 192, 320, 64, "bf16", tuple(range(30, 60))),
+]
+
+
+@pytest.mark.parametrize("R,d,de,E,dtype,empty", CASES)
+def test_grouped_ffn_against_oracle(moe, R, d, de, E, dtype, empty):
+    announce(f"ffn R={R} d={d} de={de} E={E} {dtype} empty={len(empty)}")
+    x_perm = make_dense((R, d), 1.0, seed=6, tag=1, device="cuda", dtype=dtype)
+    W1 = make_dense((E, d, de), d ** -0.5, seed=6, tag=2, device="cuda", dtype=dtype)
+    W2 = make_dense((E, de, d), de ** -0.5, seed=6, tag=3, device="cuda", dtype=dtype)
+    off = make_group_offsets(E, R, seed=6, empty=empty)
+    y = run_ffn(moe, R, d, de, E, dtype, x_perm, off.cuda(), W1, W2)
+    ref = oracle_ffn(dtype, x_perm, off, W1, W2)
+    err = rel_err(f64(y), ref)
+    print(f"ffn R={R} d={d} de={de} E={E} {dtype}: rel err {err:.3e}")
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+def test_every_tile_shape(moe, tile):
+    """Each bf16 block tile the launcher can choose, on ragged groups with
+    empty experts and rows that are not a multiple of any tile."""
+    R, d, de, E = 1299, 512, 768, 6
+    announce(f"ffn tile {tile}")
+    x_perm = make_dense((R, d), 1.0, seed=7, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=7, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=7, tag=3, device="cuda")
+    off = make_group_offsets(E, R, seed=7, empty=(1,))
+    os.environ["MOE_GEMM_TILE"] = tile
+    try:
+        y = run_ffn(moe, R, d, de, E, "bf16", x_perm, off.cuda(), W1, W2)
+    finally:
+        del os.environ["MOE_GEMM_TILE"]
+    ref = oracle_ffn("bf16", x_perm, off, W1, W2)
+    assert rel_err(f64(y), ref) <= TOL_BF16
+
+
+def test_rows_past_offsets_end_untouched(moe):
+    """Rows at or beyond offsets[E] belong to no expert and keep their contents."""
+    R, d, de, E = 500, 128, 128, 4
+    announce("ffn rows past end")
+    x_perm = make_dense((R, d), 1.0, seed=8, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=8, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=8, tag=3, device="cuda")
+    off = make_group_offsets(E, 420, seed=8)
+    y = run_ffn(moe, R, d, de, E, "bf16", x_perm, off.cuda(), W1, W2)
+    assert torch.isnan(y[420:].float()).all()
+    ref = oracle_ffn("bf16", x_perm[:420], off, W1, W2)
+    assert rel_err(f64(y[:420]), ref) <= TOL_BF16
