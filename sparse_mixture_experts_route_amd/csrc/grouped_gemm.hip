@@ -8,24 +8,31 @@
 // with act = GELU_tanh for the first expert GEMM and identity for the second.
 //
 // bf16 path (gfx950 matrix cores):
-//   * v_mfma_f32_32x32x16_bf16, float32 accumulators, 64-wide wavefronts;
-//   * block tile BM x BN, K step 64, LDS double buffer; each wave owns a
-//     (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA tiles;
-//   * both operands sit in LDS K-contiguous ([row][64] bf16, 128 B per row)
-//     with the 16-byte chunk index XOR-ed by (row & 7), so the 8 lanes of a
-//     16-byte LDS access phase hit 8 different chunk positions;
-//   * B arrives N-contiguous from HBM; each thread loads an 8(k) x 8(n)
-//     sub-block (eight 16-byte row pieces) and transposes it in registers
-//     before the LDS store;
+//   * v_mfma_f32_32x32x16_bf16 with float32 accumulators; block tile BM x BN,
+//     K step 64, four waves in a 2x2 grid, each owning (BM/2) x (BN/2);
+//   * operands go HBM -> LDS with global_load_lds_dwordx4 (no register
+//     staging): every lane of a wave writes 16 bytes to consecutive LDS
+//     slots, and the lane's global address is chosen so that the slot holds
+//     the swizzled piece;
+//   * A sits K-contiguous in LDS ([row][64] bf16, 128 B per row) with the
+//     16-byte chunk index XOR-ed by (row & 7); fragments are ds_read_b128;
+//   * B stays N-contiguous in LDS ([k][BN]) with the 16-byte chunk index
+//     XOR-ed by 2*(k & 3); fragments are read with ds_read_b64_tr_b16, which
+//     hands each lane 4 consecutive k of one column (two reads give the 8 k
+//     an MFMA lane needs), so no transpose pass is needed anywhere;
+//   * two LDS stages: the loads of stage s+2 are issued right after the one
+//     barrier of step s, fragments of the next K sub-step are read while the
+//     MFMAs of the current one run (two fragment register sets);
 //   * operands are passed to the MFMA as (B, A), so each lane's accumulators
 //     hold 4 consecutive output columns of one row: the epilogue applies
 //     GELU in float32, rounds to bf16 and stores 8 bytes per group;
-//   * the tile of a block is found on the device from offsets[] (tiles of
-//     expert e = ceil(rows_e / BM), enumerated expert by expert), so no host
-//     synchronisation on the routing is needed; empty groups own no tiles;
-//   * blocks are renumbered so that each XCD (the hardware deals blocks to
-//     the 8 XCDs round robin) works on a contiguous run of tiles, which share
-//     A rows and expert weights in that XCD's L2.
+//   * persistent blocks (one per CU): every block derives the tile list from
+//     offsets[] on the device (expert by expert; inside an expert, n-tile
+//     major and m-tile minor, so the tiles sharing an expert's weight slab
+//     run side by side). The list is cut into 8 contiguous ranges, one per
+//     XCD (the hardware deals blocks to the XCDs round robin), so each XCD's
+//     L2 serves the experts it works on. Empty groups own no tiles, and no
+//     host synchronisation on the routing is needed.
 // float32 path: a plain LDS-tiled FMA kernel (the fp32 workload is small).
 #include <stdlib.h>
 #include <string.h>
@@ -37,7 +44,51 @@ namespace moe {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
 constexpr int BK = 64;  // K step (bf16 path)
+// dword 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base address, stride 0, byte range `bytes` (loads at
+// or past it return zero), made wave-uniform.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kBufferFlags;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS: lane i
+// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address lds.
+// Issued as inline assembly so that the compiler does not wait on it before
+// unrelated LDS reads; the caller waits (vmcnt) before the barrier that
+// publishes the data.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a shared-memory pointer, made wave-uniform
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)p);
+}
 
 // Locate the m-tile `m_tile` in the expert-by-expert tile enumeration.
 // Writes {expert, first row, end row} to info (expert -1 when past the end).
@@ -87,165 +138,239 @@ __device__ __forceinline__ void find_tile(const int32_t* __restrict__ offsets, i
   __syncthreads();
 }
 
-__device__ __forceinline__ int xcd_remap(int nblk) {
-  // blocks are dealt to the 8 XCDs round robin; give XCD x the run [x*n/8, (x+1)*n/8)
-  return (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+// Tile list of the bf16 path: tstart[e] = first tile of expert e (exclusive
+// prefix over experts of m_tiles(e) * n_tiles), tstart[E] = total;
+// mtiles[e] = ceil(rows_e / BM). Computed by wave 0, shared through LDS.
+template <int BM>
+__device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets, int E, int64_t R,
+                                                int n_tiles, int* tstart, int* mtiles) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int cnt[4];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      int c = 0;
+      if (e < E) {
+        const int64_t lo = max((int64_t)offsets[e], (int64_t)0), hi = min((int64_t)offsets[e + 1], R);
+        c = hi > lo ? (int)ceil_div(hi - lo, BM) : 0;
+        mtiles[e] = c;
+      }
+      cnt[i] = c * n_tiles;
+      local += cnt[i];
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < E) tstart[e] = run;
+      run += cnt[i];
+    }
+    if (lane == kWave - 1) tstart[E] = incl;
+  }
+  __syncthreads();
 }
 
-template <int BM, int BN, int WM, int WN, bool GELU>
-__global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
-    const bf16_bits* __restrict__ A, const int32_t* __restrict__ offsets, const bf16_bits* __restrict__ B,
-    bf16_bits* __restrict__ C, int64_t R, int K, int N, int E, int n_tiles, int grid_tiles) {
-  constexpr int NT = WM * WN * kWave;
-  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+template <int BM, int BN, bool GELU>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const bf16_bits* __restrict__ B,
+                                                           bf16_bits* __restrict__ C, int64_t R, int K, int N,
+                                                           int E, int n_tiles) {
+  constexpr int NW = 4;                        // waves, 2 x 2
+  constexpr int WTM = BM / 2, WTN = BN / 2;    // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
-  constexpr int A_ITERS = BM * (BK / 8) / NT;  // 16-byte A pieces per thread per K step
-  constexpr int B_SUBS = (BK / 8) * (BN / 8);  // 8x8 sub-blocks of a B tile
-  constexpr int B_ITERS = (B_SUBS + NT - 1) / NT;
-  static_assert(BM * (BK / 8) % NT == 0, "A tile must split evenly over the block");
-  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
+  constexpr int A_STAGE = BM * BK * 2;         // bytes
+  constexpr int B_STAGE = BK * BN * 2;
+  constexpr int STAGE = A_STAGE + B_STAGE;
+  constexpr int A_LD = A_STAGE / 1024 / NW;    // 1 KB direct-to-LDS loads per wave per stage
+  constexpr int B_LD = B_STAGE / 1024 / NW;
+  constexpr int B_ROW = BN * 2;                // bytes per k row of a B stage
+  constexpr int B_SLOTS = BN / 8;              // 16-byte slots per k row
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the load split");
 
-  __shared__ __attribute__((aligned(16))) bf16_bits As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_bits Bs[2][BN * BK];
-  __shared__ int s_info[3];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ int s_tstart[257];
+  __shared__ int s_mtiles[256];
 
-  const int bid = xcd_remap(gridDim.x);
-  if (bid >= grid_tiles) return;
-  const int m_tile = bid / n_tiles, n_tile = bid % n_tiles;
-  find_tile<BM>(offsets, E, R, m_tile, s_info);
-  const int e = s_info[0];
-  if (e < 0) return;
-  const int64_t row0 = s_info[1], row_end = s_info[2];
-  if (row0 >= row_end) return;
-  const int n0 = n_tile * BN;
-  const bf16_bits* __restrict__ Be = B + (int64_t)e * K * N;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  build_tile_list<BM>(offsets, E, R, n_tiles, s_tstart, s_mtiles);
+  const int total = s_tstart[E];
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+  // contiguous share of the tile list for this block's XCD
+  const int xcd = blockIdx.x % 8, nb = gridDim.x / 8, j = blockIdx.x / 8;
+  const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
 
-  // global -> LDS addressing
-  const bf16_bits* a_src[A_ITERS];
-  int a_dst[A_ITERS];
+  lds_char* const lds = (lds_char*)smem;
+  const uint32_t lds_base = lds_addr(smem);
+  const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+
+  // per-lane LDS read offsets (bytes, within a stage)
+  int a_rd[TM];
 #pragma unroll
-  for (int i = 0; i < A_ITERS; ++i) {
-    const int q = tid + NT * i, row = q >> 3, kc = q & 7;
-    const int64_t grow = min(row0 + row, row_end - 1);
-    a_src[i] = A + grow * K + kc * 8;
-    a_dst[i] = row * BK + ((kc ^ (row & 7)) << 3);
-  }
-  const bf16_bits* b_src[B_ITERS];
-  int b_ng[B_ITERS], b_kg[B_ITERS];
-  bool b_on[B_ITERS];
+  for (int mi = 0; mi < TM; ++mi) a_rd[mi] = (wm0 + mi * 32 + (lane & 31)) * 128;
+  int a_x[4];
 #pragma unroll
-  for (int i = 0; i < B_ITERS; ++i) {
-    const int s = tid + NT * i;
-    b_on[i] = s < B_SUBS;
-    const int kg = s & 7, ng = (s >> 3) % (BN / 8);
-    const int n = min(n0 + ng * 8, N - 8);
-    b_src[i] = Be + (int64_t)(kg * 8) * N + n;
-    b_ng[i] = ng;
-    b_kg[i] = kg;
+  for (int ks = 0; ks < 4; ++ks) a_x[ks] = (((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 4);
+  // B: lane q of its 16-lane group reads row (q >> 2) of a 4-row block, columns 4*(q & 3)..+3;
+  // lanes 32..63 take the upper 8 k of each 16-k sub-step
+  const int q = lane & 15, g = lane >> 4;
+  int b_rd[TN];
+#pragma unroll
+  for (int ni = 0; ni < TN; ++ni) {
+    const int col = wn0 + ni * 32 + (g & 1) * 16 + (q & 3) * 4;
+    const int kr = q >> 2;  // == k & 3 for every k this lane reads
+    b_rd[ni] = A_STAGE + ((g >> 1) * 8 + kr) * B_ROW + (((col >> 3) ^ (2 * kr)) << 4) + (col & 7) * 2;
   }
 
-  u32x4 ra[A_ITERS];
-  u32x4 rb[B_ITERS][8];
+  for (int t = lo + j; t < hi; t += nb) {
+    // ---- locate the tile: expert e with tstart[e] <= t < tstart[e+1] (upper bound - 1)
+    int a0 = 0, a1 = E;
+    while (a1 - a0 > 1) {
+      const int mid = (a0 + a1) >> 1;
+      if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(a0);
+    const int local = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
+    const int mt = __builtin_amdgcn_readfirstlane(s_mtiles[e]);
+    const int n_tile = local / mt, m_idx = local - n_tile * mt;
+    const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(offsets[e]) + (int64_t)m_idx * BM;
+    const int64_t row_end = min((int64_t)__builtin_amdgcn_readfirstlane(offsets[e + 1]), R);
+    const int n0 = n_tile * BN;
 
-  auto gload = [&](int kt) {
-    const int64_t koff = (int64_t)kt * BK;
+    // ---- buffer descriptors of this tile (wave-uniform) and per-lane byte offsets.
+    // A: rows row0.. of the group; rows past the group's end fall outside the
+    // descriptor's range and read as zero. B: the expert's [K, N] slab.
+    const i32x4 rsA = buffer_rsrc(A + row0 * K, (uint32_t)((row_end - row0) * K * 2));
+    const i32x4 rsB = buffer_rsrc(B + (int64_t)e * K * N, (uint32_t)((int64_t)K * N * 2));
+    uint32_t a_off[A_LD];
 #pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) ra[i] = *(const u32x4*)(a_src[i] + koff);
+    for (int i = 0; i < A_LD; ++i) {
+      const int p = (wave * A_LD + i) * 64 + lane;  // LDS slot
+      const int row = p >> 3, c = (p & 7) ^ (row & 7);
+      a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
+    }
+    uint32_t b_off[B_LD];
 #pragma unroll
-    for (int i = 0; i < B_ITERS; ++i)
-      if (b_on[i]) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rb[i][r] = *(const u32x4*)(b_src[i] + (koff + r) * N);
-      }
-  };
+    for (int i = 0; i < B_LD; ++i) {
+      const int p = (wave * B_LD + i) * 64 + lane;
+      const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (2 * (k & 3));
+      b_off[i] = (uint32_t)(k * N + n0 + c * 8) * 2u;
+    }
 
-  auto sts = [&](int buf) {
+    auto issue = [&](int kt, int buf) {
+      const uint32_t sa = (uint32_t)kt * BK * 2, sb = (uint32_t)kt * BK * N * 2;
+      const uint32_t la = lds_base + buf * STAGE + wave * A_LD * 1024;
+      const uint32_t lb = lds_base + buf * STAGE + A_STAGE + wave * B_LD * 1024;
 #pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) *(u32x4*)(&As[buf][a_dst[i]]) = ra[i];
+      for (int i = 0; i < A_LD; ++i) buffer_load_lds16(rsA, a_off[i], sa, la + i * 1024);
 #pragma unroll
-    for (int i = 0; i < B_ITERS; ++i)
-      if (b_on[i]) {
-        // 8x8 transpose: rb[r] holds k = r for n = 0..7; w holds n = c for k = 0..7
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          u32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = rb[i][2 * j][c >> 1], hi = rb[i][2 * j + 1][c >> 1];
-            w[j] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-          }
-          const int n = b_ng[i] * 8 + c;
-          *(u32x4*)(&Bs[buf][n * BK + ((b_kg[i] ^ c) << 3)]) = w;
-        }
-      }
-  };
+      for (int i = 0; i < B_LD; ++i) buffer_load_lds16(rsB, b_off[i], sb, lb + i * 1024);
+    };
 
-  f32x16 acc[TM][TN];
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto read_frags = [&](int buf, int ks, int set) {
+      lds_char* const st = lds + buf * STAGE;
 #pragma unroll
-  for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-
-  const int nk = K / BK;
-  gload(0);
-  sts(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi) {
-        const int row = wm0 + mi * 32 + (lane & 31);
-        af[mi] = *(const bf16x8*)(&As[cur][row * BK + ((kc ^ (row & 7)) << 3)]);
-      }
+      for (int mi = 0; mi < TM; ++mi) fa[set][mi] = *(lds_bf16x8*)(st + a_rd[mi] + a_x[ks]);
 #pragma unroll
       for (int ni = 0; ni < TN; ++ni) {
-        const int n = wn0 + ni * 32 + (lane & 31);
-        bfr[ni] = *(const bf16x8*)(&Bs[cur][n * BK + ((kc ^ (n & 7)) << 3)]);
+        lds_char* const p0 = st + ks * 16 * B_ROW + b_rd[ni];
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * B_ROW));
+        const s16x8 v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        fb[set][ni] = __builtin_bit_cast(bf16x8, v);
       }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+    auto mfma_range = [&](int set, int lo_i, int hi_i) {
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sts(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds row (lane & 31) of each MFMA tile, columns 8g + 4*(lane>>5) + 0..3
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi) {
-    const int64_t row = row0 + wm0 + mi * 32 + (lane & 31);
-    if (row >= row_end) continue;
-    bf16_bits* crow = C + row * N;
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn0 + ni * 32 + 8 * g + 4 * (lane >> 5);
-        if (n >= N) continue;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = acc[mi][ni][4 * g + q];
-          if (GELU) v[q] = gelu_tanh(v[q]);
+        for (int ni = 0; ni < TN; ++ni) {
+          const int idx = mi * TN + ni;
+          if (idx >= lo_i && idx < hi_i)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
         }
-        u32x2 o;
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
-        *(u32x2*)(crow + n) = o;
+    };
+
+    const int nk = K / BK;
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    wait_vmem_all();
+    __syncthreads();
+    read_frags(0, 0, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      // each sub-step: issue the next fragments' LDS reads, then the MFMAs of the current ones
+      read_frags(cur, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_range(0, 0, TM * TN);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_range(1, 0, TM * TN);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_range(0, 0, TM * TN);
+      __builtin_amdgcn_sched_barrier(0);
+      // last sub-step: half the MFMAs, then the step's barrier, then the next stage's first fragments
+      mfma_range(1, 0, TM * TN / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        wait_vmem_all();  // this wave's stage kt+1 loads have landed in LDS
+        __syncthreads();  // ... and every wave's; every wave is done reading buffer cur
+        if (kt + 2 < nk) issue(kt + 2, cur);
+        read_frags(cur ^ 1, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_range(1, TM * TN / 2, TM * TN);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();  // every wave is done with both buffers before the next tile's loads
+
+    // ---- epilogue: lane holds row (lane & 31) of each MFMA tile, columns 8g + 4*(lane>>5) + 0..3
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int64_t row = row0 + wm0 + mi * 32 + (lane & 31);
+      if (row >= row_end) continue;
+      bf16_bits* crow = C + row * N;
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5);
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            v[qq] = acc[mi][ni][4 * gq + qq];
+            if (GELU) v[qq] = gelu_tanh(v[qq]);
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(v[0], v[1]);
+          o[1] = pack_bf16x2(v[2], v[3]);
+          *(u32x2*)(crow + n) = o;
+        }
+    }
   }
 }
 
@@ -309,32 +434,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- host side
 
-struct TileCfg {
-  int bm, bn;
-};
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, int64_t R, int K, int N,
                        int E, bool gelu, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
   const int64_t m_tiles = (R + (int64_t)E * (BM - 1)) / BM;  // >= sum over experts of ceil(rows_e / BM)
-  const int64_t grid_tiles = m_tiles * n_tiles;
-  const int64_t blocks = ceil_div(grid_tiles, 8) * 8;
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t tiles_ub = m_tiles * n_tiles;
+  if (tiles_ub > INT32_MAX) return hipErrorInvalidValue;
+  // persistent grid: one block per CU, a multiple of 8 so every XCD holds the same number of blocks
+  const int64_t cus = device_cus() / 8 * 8;
+  const int64_t grid = max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, cus));
   if (gelu)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), dim3((unsigned)blocks), dim3(WM * WN * kWave),
-                       0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E,
-                       n_tiles, (int)grid_tiles);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), dim3((unsigned)blocks),
-                       dim3(WM * WN * kWave), 0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B,
-                       (bf16_bits*)C, R, K, N, E, n_tiles, (int)grid_tiles);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
   return hipGetLastError();
 }
 
-// Pick the block tile from the expected tile count: fewer, larger tiles
-// use the matrix cores better, but a last partial wave of tiles over the 256
-// CUs and padding rows of half-empty M tiles cost time.
+// Block tile for a GEMM: fewer, larger tiles use the matrix cores better, but
+// a last partial round of tiles over the CUs and padding rows of half-empty
+// M tiles cost time. MOE_GEMM_TILE=256x256|256x128|128x128 forces a shape.
 int pick_tile(int64_t R, int N, int E) {
   const char* force = getenv("MOE_GEMM_TILE");
   if (force && force[0]) {
@@ -342,17 +474,18 @@ int pick_tile(int64_t R, int N, int E) {
     if (!strcmp(force, "256x128")) return 1;
     if (!strcmp(force, "128x128")) return 2;
   }
-  const TileCfg cfgs[3] = {{256, 256}, {256, 128}, {128, 128}};
-  const double tile_eff[3] = {1.0, 0.92, 0.80};  // relative MFMA efficiency of one busy CU
+  const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
+  const double tile_eff[3] = {1.0, 0.9, 0.75};  // relative MFMA efficiency of one busy CU
+  const double cus = device_cus();
   int best = 0;
   double best_score = -1.0;
   for (int c = 0; c < 3; ++c) {
-    const double m_tiles = (double)R / cfgs[c].bm + 0.5 * E;
-    const double tiles = m_tiles * ceil_div(N, cfgs[c].bn);
-    const double waves = tiles / 256.0;
-    const double wave_eff = tiles / (256.0 * (double)(int64_t)(waves + 0.999));
-    const double pad_eff = (double)R / (m_tiles * cfgs[c].bm);
-    const double score = tile_eff[c] * wave_eff * pad_eff;
+    const double m_tiles = (double)R / bm[c] + 0.5 * E;
+    const double tiles = m_tiles * ceil_div(N, bn[c]);
+    const double rounds = tiles / cus;
+    const double round_eff = tiles / (cus * (double)(int64_t)(rounds + 0.999));
+    const double pad_eff = (double)R / (m_tiles * bm[c]);
+    const double score = tile_eff[c] * round_eff * pad_eff;
     if (score > best_score) {
       best_score = score;
       best = c;
@@ -380,11 +513,11 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
   }
   switch (pick_tile(R, N, E)) {
     case 0:
-      return launch_bf16<256, 256, 2, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256>(A, offsets, B, C, R, K, N, E, gelu, s);
     case 1:
-      return launch_bf16<256, 128, 2, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 128>(A, offsets, B, C, R, K, N, E, gelu, s);
     default:
-      return launch_bf16<128, 128, 2, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<128, 128>(A, offsets, B, C, R, K, N, E, gelu, s);
   }
 }
 
