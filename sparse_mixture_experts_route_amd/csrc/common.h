@@ -14,6 +14,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -24,17 +26,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// two float32 -> packed bfloat16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// tanh-form GELU: u/2 * (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
-// tanh z = 1 - 2 / (exp(2z) + 1), which saturates correctly at both ends.
+// tanh-form GELU: u/2 * (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3).
+// Since (1 + tanh z) / 2 = 1 / (1 + e^(-2z)), this is u / (1 + 2^(-2 z log2 e)),
+// evaluated with the hardware exp2 and reciprocal (no division). Both ends
+// saturate correctly: a huge exponent gives 1/inf = 0, a tiny one 1/1.
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float z = c * (u + 0.044715f * u * u * u);
-  float t = 1.0f - 2.0f / (__expf(2.0f * z) + 1.0f);
-  return 0.5f * u * (1.0f + t);
+  const float k0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float k1 = k0 * 0.044715f;
+  const float t = u * fmaf(k1, u * u, k0);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // Order-preserving map of a float32 to uint32 (larger float -> larger key);

@@ -15,7 +15,10 @@
 //     slots, and the lane's global address is chosen so that the slot holds
 //     the swizzled piece;
 //   * A sits K-contiguous in LDS ([row][64] bf16, 128 B per row) with the
-//     16-byte chunk index XOR-ed by (row & 7); fragments are ds_read_b128;
+//     16-byte chunk index XOR-ed by ((row >> 1) & 7): the LDS has 64 banks (a
+//     256-byte period, two rows), and the 16 lanes served together read 16
+//     consecutive rows, which this spreads over all 64 banks; fragments are
+//     ds_read_b128;
 //   * B stays N-contiguous in LDS ([k][BN]) with the 16-byte chunk index
 //     XOR-ed by 2*(k & 3); fragments are read with ds_read_b64_tr_b16, which
 //     hands each lane 4 consecutive k of one column (two reads give the 8 k
@@ -51,7 +54,6 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-constexpr int BK = 64;  // K step (bf16 path)
 // dword 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -83,7 +85,6 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t voff, uin
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS byte address of a shared-memory pointer, made wave-uniform
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -178,25 +179,40 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   __syncthreads();
 }
 
-template <int BM, int BN, bool GELU>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const bf16_bits* __restrict__ B,
-                                                           bf16_bits* __restrict__ C, int64_t R, int K, int N,
-                                                           int E, int n_tiles) {
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block tile BM x BN over K steps of BK, a ring of S LDS stages, OCC blocks per CU.
+template <int BM, int BN, int BK, int S, int OCC, bool GELU>
+__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const bf16_bits* __restrict__ B,
+                                                             bf16_bits* __restrict__ C, int64_t R, int K, int N,
+                                                             int E, int n_tiles) {
   constexpr int NW = 4;                        // waves, 2 x 2
   constexpr int WTM = BM / 2, WTN = BN / 2;    // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
-  constexpr int A_STAGE = BM * BK * 2;         // bytes
-  constexpr int B_STAGE = BK * BN * 2;
+  constexpr int KS = BK / 16;                  // MFMA K sub-steps per stage
+  constexpr int A_ROW = BK * 2;                // bytes per A row of a stage
+  constexpr int A_CH = BK / 8;                 // 16-byte chunks per A row
+  constexpr int A_STAGE = BM * A_ROW;
+  constexpr int B_ROW = BN * 2;                // bytes per k row of a B stage
+  constexpr int B_SLOTS = BN / 8;              // 16-byte slots per k row
+  constexpr int B_STAGE = BK * B_ROW;
   constexpr int STAGE = A_STAGE + B_STAGE;
   constexpr int A_LD = A_STAGE / 1024 / NW;    // 1 KB direct-to-LDS loads per wave per stage
   constexpr int B_LD = B_STAGE / 1024 / NW;
-  constexpr int B_ROW = BN * 2;                // bytes per k row of a B stage
-  constexpr int B_SLOTS = BN / 8;              // 16-byte slots per k row
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the load split");
+  constexpr int NL = A_LD + B_LD;
+  // A: 16 consecutive rows are read together and span 16 * A_ROW bytes; the
+  // chunk swizzle makes them cover the 64 banks (256 bytes) exactly once
+  constexpr int A_RPP = 256 / A_ROW;           // rows per 256-byte bank period
+  static_assert(A_LD >= 1 && B_LD >= 1 && KS >= 2 && S >= 2, "unsupported tile");
+  static_assert(A_RPP * A_CH == 16, "A swizzle assumes 16 chunks per bank period");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   __shared__ int s_tstart[257];
   __shared__ int s_mtiles[256];
 
@@ -216,10 +232,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const bf16_bits* __re
   // per-lane LDS read offsets (bytes, within a stage)
   int a_rd[TM];
 #pragma unroll
-  for (int mi = 0; mi < TM; ++mi) a_rd[mi] = (wm0 + mi * 32 + (lane & 31)) * 128;
-  int a_x[4];
+  for (int mi = 0; mi < TM; ++mi) a_rd[mi] = (wm0 + mi * 32 + (lane & 31)) * A_ROW;
+  int a_x[KS];
+  {
+    const int r = lane & 31;  // row within an MFMA tile; tiles start at multiples of 32
+    const int sw = (r / A_RPP) & (A_CH - 1);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) a_x[ks] = (((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 4);
+    for (int ks = 0; ks < KS; ++ks) a_x[ks] = ((ks * 2 + (lane >> 5)) ^ sw) << 4;
+  }
   // B: lane q of its 16-lane group reads row (q >> 2) of a 4-row block, columns 4*(q & 3)..+3;
   // lanes 32..63 take the upper 8 k of each 16-k sub-step
   const int q = lane & 15, g = lane >> 4;
@@ -231,67 +251,110 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const bf16_bits* __re
     b_rd[ni] = A_STAGE + ((g >> 1) * 8 + kr) * B_ROW + (((col >> 3) ^ (2 * kr)) << 4) + (col & 7) * 2;
   }
 
-  for (int t = lo + j; t < hi; t += nb) {
-    // ---- locate the tile: expert e with tstart[e] <= t < tstart[e+1] (upper bound - 1)
+  // ---- per-tile state: tile coordinates, buffer descriptors, per-lane load offsets
+  struct Tile {
+    int e, n0;
+    int64_t row0, row_end;
+    i32x4 rsA, rsB;
+  };
+  auto locate = [&](int t) {
+    // expert e with tstart[e] <= t < tstart[e+1] (upper bound - 1)
     int a0 = 0, a1 = E;
     while (a1 - a0 > 1) {
       const int mid = (a0 + a1) >> 1;
       if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
     }
-    const int e = __builtin_amdgcn_readfirstlane(a0);
-    const int local = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
-    const int mt = __builtin_amdgcn_readfirstlane(s_mtiles[e]);
+    Tile tl;
+    tl.e = __builtin_amdgcn_readfirstlane(a0);
+    const int local = t - __builtin_amdgcn_readfirstlane(s_tstart[tl.e]);
+    const int mt = __builtin_amdgcn_readfirstlane(s_mtiles[tl.e]);
     const int n_tile = local / mt, m_idx = local - n_tile * mt;
-    const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(offsets[e]) + (int64_t)m_idx * BM;
-    const int64_t row_end = min((int64_t)__builtin_amdgcn_readfirstlane(offsets[e + 1]), R);
-    const int n0 = n_tile * BN;
-
-    // ---- buffer descriptors of this tile (wave-uniform) and per-lane byte offsets.
+    tl.row0 = (int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e]) + (int64_t)m_idx * BM;
+    tl.row_end = min((int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e + 1]), R);
+    tl.n0 = n_tile * BN;
     // A: rows row0.. of the group; rows past the group's end fall outside the
     // descriptor's range and read as zero. B: the expert's [K, N] slab.
-    const i32x4 rsA = buffer_rsrc(A + row0 * K, (uint32_t)((row_end - row0) * K * 2));
-    const i32x4 rsB = buffer_rsrc(B + (int64_t)e * K * N, (uint32_t)((int64_t)K * N * 2));
-    uint32_t a_off[A_LD];
+    tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)((tl.row_end - tl.row0) * K * 2));
+    tl.rsB = buffer_rsrc(B + (int64_t)tl.e * K * N, (uint32_t)((int64_t)K * N * 2));
+    return tl;
+  };
+  // per-lane byte offsets of the direct-to-LDS loads (A part does not depend on the tile)
+  uint32_t a_off[A_LD];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int p = (wave * A_LD + i) * 64 + lane;  // LDS slot
-      const int row = p >> 3, c = (p & 7) ^ (row & 7);
-      a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
-    }
-    uint32_t b_off[B_LD];
+  for (int i = 0; i < A_LD; ++i) {
+    const int p = (wave * A_LD + i) * 64 + lane;  // LDS slot
+    const int row = p / A_CH, c = (p % A_CH) ^ ((row / A_RPP) & (A_CH - 1));
+    a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
+  }
+  uint32_t b_off0[B_LD];  // for n0 = 0
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int p = (wave * B_LD + i) * 64 + lane;
-      const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (2 * (k & 3));
-      b_off[i] = (uint32_t)(k * N + n0 + c * 8) * 2u;
-    }
+  for (int i = 0; i < B_LD; ++i) {
+    const int p = (wave * B_LD + i) * 64 + lane;
+    const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (2 * (k & 3));
+    b_off0[i] = (uint32_t)(k * N + c * 8) * 2u;
+  }
 
-    auto issue = [&](int kt, int buf) {
-      const uint32_t sa = (uint32_t)kt * BK * 2, sb = (uint32_t)kt * BK * N * 2;
-      const uint32_t la = lds_base + buf * STAGE + wave * A_LD * 1024;
-      const uint32_t lb = lds_base + buf * STAGE + A_STAGE + wave * B_LD * 1024;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) buffer_load_lds16(rsA, a_off[i], sa, la + i * 1024);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) buffer_load_lds16(rsB, b_off[i], sb, lb + i * 1024);
-    };
+  // load `i` (0 .. NL-1) of stage kt into ring buffer buf
+  auto issue_one = [&](const Tile& tl, int kt, int buf, int i) {
+    const uint32_t st = lds_base + buf * STAGE;
+    if (i < A_LD)
+      buffer_load_lds16(tl.rsA, a_off[i], (uint32_t)kt * BK * 2, st + (wave * A_LD + i) * 1024);
+    else
+      buffer_load_lds16(tl.rsB, b_off0[i - A_LD] + (uint32_t)tl.n0 * 2, (uint32_t)kt * BK * N * 2,
+                        st + A_STAGE + (wave * B_LD + i - A_LD) * 1024);
+  };
 
-    bf16x8 fa[2][TM], fb[2][TN];
-    auto read_frags = [&](int buf, int ks, int set) {
-      lds_char* const st = lds + buf * STAGE;
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi) fa[set][mi] = *(lds_bf16x8*)(st + a_rd[mi] + a_x[ks]);
-#pragma unroll
-      for (int ni = 0; ni < TN; ++ni) {
-        lds_char* const p0 = st + ks * 16 * B_ROW + b_rd[ni];
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * B_ROW));
-        const s16x8 v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        fb[set][ni] = __builtin_bit_cast(bf16x8, v);
+  bf16x8 fa[2][TM], fb[2][TN];
+  constexpr int NR = TM + 2 * TN;  // LDS reads per fragment set
+  // read `r` (0 .. NR-1) of the fragments of sub-step ks of ring buffer buf into set
+  auto read_one = [&](int buf, int ks, int set, int r) {
+    lds_char* const st = lds + buf * STAGE;
+    if (r < TM) {
+      fa[set][r] = *(lds_bf16x8*)(st + a_rd[r] + a_x[ks]);
+    } else {
+      const int ni = (r - TM) >> 1, hi = (r - TM) & 1;
+      lds_char* const p0 = st + ks * 16 * B_ROW + b_rd[ni] + hi * 4 * B_ROW;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+      s16x8 w = __builtin_bit_cast(s16x8, fb[set][ni]);
+      if (hi) {
+        w[4] = v[0]; w[5] = v[1]; w[6] = v[2]; w[7] = v[3];
+      } else {
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
       }
-    };
+      fb[set][ni] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
 
-    f32x16 acc[TM][TN];
+  f32x16 acc[TM][TN];
+  auto mfma_one = [&](int set, int idx) {
+    const int mi = idx / TN, ni = idx % TN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
+  };
+
+  const int nk = K / BK;
+  constexpr int NM = TM * TN;  // MFMAs per sub-step
+  constexpr int H = NM / 2;    // MFMAs of the last sub-step before the step's barrier
+  // fragment reads issued after each MFMA: a set's reads all go out in the first
+  // half of the sub-step, so they have landed when the next sub-step starts
+  constexpr int RPM = (NR + NM / 2 - 1) / (NM / 2);
+
+  int t = lo + j;
+  Tile tl;
+  if (t < hi) {
+    tl = locate(t);
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2)
+      if (s2 < nk)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) issue_one(tl, s2, s2, i);
+  }
+
+  for (; t < hi; t += nb) {
+    // ---- stages 0 .. S-1 of this tile were issued; wait for all of them (and older stores)
+    wait_vmem<0>();
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
@@ -299,65 +362,82 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const bf16_bits* __re
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-    auto mfma_range = [&](int set, int lo_i, int hi_i) {
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-          const int idx = mi * TN + ni;
-          if (idx >= lo_i && idx < hi_i)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
-        }
-    };
-
-    const int nk = K / BK;
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    wait_vmem_all();
-    __syncthreads();
-    read_frags(0, 0, 0);
-
+    int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      // each sub-step: issue the next fragments' LDS reads, then the MFMAs of the current ones
-      read_frags(cur, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_range(0, 0, TM * TN);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(cur, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_range(1, 0, TM * TN);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(cur, 3, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_range(0, 0, TM * TN);
-      __builtin_amdgcn_sched_barrier(0);
-      // last sub-step: half the MFMAs, then the step's barrier, then the next stage's first fragments
-      mfma_range(1, 0, TM * TN / 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) {
-        wait_vmem_all();  // this wave's stage kt+1 loads have landed in LDS
-        __syncthreads();  // ... and every wave's; every wave is done reading buffer cur
-        if (kt + 2 < nk) issue(kt + 2, cur);
-        read_frags(cur ^ 1, 0, 0);
+      // sub-steps 0 .. KS-2: MFMAs of the current fragments, one LDS read of the next set after each
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          mfma_one(ks & 1, i);
+#pragma unroll
+          for (int u = 0; u < RPM; ++u)
+            if (i * RPM + u < NR) read_one(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_range(1, TM * TN / 2, TM * TN);
-      __builtin_amdgcn_sched_barrier(0);
+      // last sub-step: H MFMAs, the step's barrier, then the rest of the MFMAs
+      // with the refill of this buffer (stage kt+S) and the next stage's first
+      // fragment reads spread between them
+      constexpr int LAST = (KS - 1) & 1;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        mfma_one(LAST, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool more = kt + 1 < nk;
+      const int nbuf = buf + 1 == S ? 0 : buf + 1;
+      if (more) {
+        // stage kt+1 must have landed; stages kt+2 .. kt+S-1 may still be in flight
+        if (kt + S - 1 < nk)
+          wait_vmem<NL * (S - 2)>();
+        else
+          wait_vmem<0>();
+        __syncthreads();  // every wave's stage kt+1 is in; every wave is done reading `buf`
+      }
+      const bool refill = kt + S < nk;
+#pragma unroll
+      for (int i = 0; i < NM - H; ++i) {
+        mfma_one(LAST, H + i);
+        constexpr int PER = (NL + NR + (NM - H) - 1) / (NM - H);  // memory ops per MFMA
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          // the next stage's first fragments first (needed soonest), then the refill loads
+          const int op = i * PER + u;
+          if (op < NR) {
+            if (more) read_one(nbuf, 0, 0, op);
+          } else if (op < NR + NL) {
+            if (refill) issue_one(tl, kt + S, buf, op - NR);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      buf = nbuf;
     }
-    __syncthreads();  // every wave is done with both buffers before the next tile's loads
+    __syncthreads();  // every wave is done with every buffer
+
+    // ---- the next tile's first stages go out before this tile's epilogue
+    const Tile cur = tl;
+    if (t + nb < hi) {
+      tl = locate(t + nb);
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2)
+        if (s2 < nk)
+#pragma unroll
+          for (int i = 0; i < NL; ++i) issue_one(tl, s2, s2, i);
+    }
 
     // ---- epilogue: lane holds row (lane & 31) of each MFMA tile, columns 8g + 4*(lane>>5) + 0..3
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
-      const int64_t row = row0 + wm0 + mi * 32 + (lane & 31);
-      if (row >= row_end) continue;
+      const int64_t row = cur.row0 + wm0 + mi * 32 + (lane & 31);
+      if (row >= cur.row_end) continue;
       bf16_bits* crow = C + row * N;
 #pragma unroll
       for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5);
+          const int n = cur.n0 + wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5);
           if (n >= N) continue;
           float v[4];
 #pragma unroll
@@ -445,28 +525,37 @@ int device_cus() {
   return cus;
 }
 
-template <int BM, int BN>
+// Tile configurations of the bf16 path.
+//   0: 256 x 256, K step 64, 2 stages (128 KB LDS), one block per CU
+//   1: 256 x 128, K step 32, 3 stages (72 KB LDS), two blocks per CU
+//   2: 128 x 128, K step 64, 2 stages (64 KB LDS), two blocks per CU
+struct TileShape {
+  int bm, bn, occ;
+};
+constexpr TileShape kShapes[3] = {{256, 256, 1}, {256, 128, 2}, {128, 128, 2}};
+
+template <int BM, int BN, int BK, int S, int OCC>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, int64_t R, int K, int N,
                        int E, bool gelu, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
   const int64_t m_tiles = (R + (int64_t)E * (BM - 1)) / BM;  // >= sum over experts of ceil(rows_e / BM)
   const int64_t tiles_ub = m_tiles * n_tiles;
   if (tiles_ub > INT32_MAX) return hipErrorInvalidValue;
-  // persistent grid: one block per CU, a multiple of 8 so every XCD holds the same number of blocks
-  const int64_t cus = device_cus() / 8 * 8;
-  const int64_t grid = max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, cus));
+  // persistent grid: OCC blocks per CU, a multiple of 8 so every XCD holds the same number of blocks
+  const int64_t slots = (int64_t)device_cus() / 8 * 8 * OCC;
+  const int64_t grid = max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, slots));
   if (gelu)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, true>), dim3((unsigned)grid), dim3(256), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, false>), dim3((unsigned)grid), dim3(256), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
   return hipGetLastError();
 }
 
 // Block tile for a GEMM: fewer, larger tiles use the matrix cores better, but
-// a last partial round of tiles over the CUs and padding rows of half-empty
-// M tiles cost time. MOE_GEMM_TILE=256x256|256x128|128x128 forces a shape.
+// a last partial round of tiles over the block slots and padding rows of
+// half-empty M tiles cost time. MOE_GEMM_TILE=256x256|256x128|128x128 forces a shape.
 int pick_tile(int64_t R, int N, int E) {
   const char* force = getenv("MOE_GEMM_TILE");
   if (force && force[0]) {
@@ -474,17 +563,17 @@ int pick_tile(int64_t R, int N, int E) {
     if (!strcmp(force, "256x128")) return 1;
     if (!strcmp(force, "128x128")) return 2;
   }
-  const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
-  const double tile_eff[3] = {1.0, 0.9, 0.75};  // relative MFMA efficiency of one busy CU
+  const double tile_eff[3] = {0.9, 1.0, 0.8};  // relative matrix-core efficiency of a busy CU
   const double cus = device_cus();
   int best = 0;
   double best_score = -1.0;
   for (int c = 0; c < 3; ++c) {
-    const double m_tiles = (double)R / bm[c] + 0.5 * E;
-    const double tiles = m_tiles * ceil_div(N, bn[c]);
-    const double rounds = tiles / cus;
-    const double round_eff = tiles / (cus * (double)(int64_t)(rounds + 0.999));
-    const double pad_eff = (double)R / (m_tiles * bm[c]);
+    const TileShape& ts = kShapes[c];
+    const double m_tiles = (double)R / ts.bm + 0.5 * E;
+    const double tiles = m_tiles * ceil_div(N, ts.bn);
+    const double rounds = tiles / (cus * ts.occ);
+    const double round_eff = rounds / (double)(int64_t)(rounds + 0.999);
+    const double pad_eff = (double)R / (m_tiles * ts.bm);
     const double score = tile_eff[c] * round_eff * pad_eff;
     if (score > best_score) {
       best_score = score;
@@ -513,11 +602,11 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
   }
   switch (pick_tile(R, N, E)) {
     case 0:
-      return launch_bf16<256, 256>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, R, K, N, E, gelu, s);
     case 1:
-      return launch_bf16<256, 128>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
     default:
-      return launch_bf16<128, 128>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
   }
 }
 
