@@ -9,33 +9,42 @@
 //
 // bf16 path (gfx950 matrix cores):
 //   * v_mfma_f32_32x32x16_bf16 with float32 accumulators; block tile BM x BN,
-//     K step 64, four waves in a 2x2 grid, each owning (BM/2) x (BN/2);
-//   * operands go HBM -> LDS with global_load_lds_dwordx4 (no register
+//     K step BK, WM x WN waves each owning (BM/WM) x (BN/WN). The default
+//     tile is 256 x 256 with 8 waves (two per SIMD): issuing a direct-to-LDS
+//     load stalls the issuing wave for tens of cycles, and the second wave on
+//     the SIMD keeps the matrix core busy meanwhile;
+//   * operands go HBM -> LDS with buffer_load_dwordx4 ... lds (no register
 //     staging): every lane of a wave writes 16 bytes to consecutive LDS
 //     slots, and the lane's global address is chosen so that the slot holds
 //     the swizzled piece;
-//   * A sits K-contiguous in LDS ([row][64] bf16, 128 B per row) with the
-//     16-byte chunk index XOR-ed by ((row >> 1) & 7): the LDS has 64 banks (a
-//     256-byte period, two rows), and the 16 lanes served together read 16
+//   * A sits K-contiguous in LDS ([row][BK] bf16) with the 16-byte chunk index
+//     XOR-ed by the row's position in its 256-byte bank period: the LDS has 64
+//     banks (a 256-byte period), and the 16 lanes served together read 16
 //     consecutive rows, which this spreads over all 64 banks; fragments are
 //     ds_read_b128;
 //   * B stays N-contiguous in LDS ([k][BN]) with the 16-byte chunk index
-//     XOR-ed by 2*(k & 3); fragments are read with ds_read_b64_tr_b16, which
-//     hands each lane 4 consecutive k of one column (two reads give the 8 k
-//     an MFMA lane needs), so no transpose pass is needed anywhere;
-//   * two LDS stages: the loads of stage s+2 are issued right after the one
-//     barrier of step s, fragments of the next K sub-step are read while the
-//     MFMAs of the current one run (two fragment register sets);
+//     XOR-ed by 4*(k & 3) (conflict-free for the reads below); fragments are
+//     read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of
+//     one column (two reads give the 8 k an MFMA lane needs), so no transpose
+//     pass is needed anywhere;
+//   * a ring of S LDS stages with one barrier per K step; fragments of the
+//     next K sub-step are read while the MFMAs of the current one run (two
+//     fragment register sets), the refill loads go out after the barrier;
 //   * operands are passed to the MFMA as (B, A), so each lane's accumulators
-//     hold 4 consecutive output columns of one row: the epilogue applies
-//     GELU in float32, rounds to bf16 and stores 8 bytes per group;
-//   * persistent blocks (one per CU): every block derives the tile list from
+//     hold 4 consecutive output columns of one row;
+//   * epilogue through LDS: GELU in float32, bf16 rounding, each wave stages
+//     its piece row-major in the idle ring and writes whole row segments with
+//     16 bytes per lane;
+//   * persistent blocks (OCC per CU): every block derives the tile list from
 //     offsets[] on the device (expert by expert; inside an expert, n-tile
 //     major and m-tile minor, so the tiles sharing an expert's weight slab
 //     run side by side). The list is cut into 8 contiguous ranges, one per
 //     XCD (the hardware deals blocks to the XCDs round robin), so each XCD's
 //     L2 serves the experts it works on. Empty groups own no tiles, and no
-//     host synchronisation on the routing is needed.
+//     host synchronisation on the routing is needed;
+//   * a small last round of long tiles is split over all of the XCD's blocks
+//     by K steps (stream-K style): float32 partial sums go to a workspace and
+//     gemm_fixup_kernel adds them in K order (deterministic) and stores.
 // float32 path: a plain LDS-tiled FMA kernel (the fp32 workload is small).
 #include <stdlib.h>
 #include <string.h>
@@ -185,15 +194,59 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Block tile BM x BN over K steps of BK, a ring of S LDS stages, OCC blocks per CU.
-template <int BM, int BN, int BK, int S, int OCC, bool GELU>
-__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
-                                                             const int32_t* __restrict__ offsets,
-                                                             const bf16_bits* __restrict__ B,
-                                                             bf16_bits* __restrict__ C, int64_t R, int K, int N,
-                                                             int E, int n_tiles) {
-  constexpr int NW = 4;                        // waves, 2 x 2
-  constexpr int WTM = BM / 2, WTN = BN / 2;    // wave tile
+// Work of one block of a persistent launch over `tiles` tiles of `nk` K steps
+// shared by `nb` blocks (index j): `full` whole tiles (tiles j, j + nb, ...),
+// then units [s0, s1) of the remaining rem * nk (tile, K step) units, counted
+// tile-major over the last `rem` tiles; they touch leftover tiles
+// r_first .. r_first + n_items - full - 1 (at most two, as rem < nb).
+// The leftover tiles are split only when they fill at most a third of a round
+// (a fuller last round runs on partly idle CUs anyway) and when the K steps it
+// saves, (nb - rem) / nb of a tile, outweigh the partial-sum traffic and the
+// fixup launch, which cost about as much as `min_steps` K steps (24 measured
+// on gfx950 with 256 x 256 tiles).
+struct SplitK {
+  int full, rem, r_first, n_items;
+  int64_t s0, s1;
+};
+
+constexpr int kSplitMinSteps = 24;
+
+__host__ __device__ __forceinline__ bool split_leftover(int rem, int nb, int nk, int min_steps) {
+  return rem > 0 && rem * 3 <= nb && (int64_t)nk * (nb - rem) >= (int64_t)min_steps * nb;
+}
+
+__device__ __forceinline__ SplitK split_k(int tiles, int nb, int j, int nk, int min_steps) {
+  SplitK r;
+  r.full = tiles / nb;
+  r.rem = tiles - r.full * nb;
+  if (!split_leftover(r.rem, nb, nk, min_steps)) {
+    r.full += j < r.rem ? 1 : 0;  // one more round of whole tiles for the first rem blocks
+    r.rem = 0;
+    r.s0 = r.s1 = 0;
+    r.r_first = 0;
+    r.n_items = r.full;
+    return r;
+  }
+  const int64_t W = (int64_t)r.rem * nk;
+  r.s0 = W * j / nb;
+  r.s1 = W * (j + 1) / nb;
+  r.r_first = r.s1 > r.s0 ? (int)(r.s0 / nk) : 0;
+  const int n_rem = r.s1 > r.s0 ? (int)((r.s1 - 1) / nk) - r.r_first + 1 : 0;
+  r.n_items = r.full + n_rem;
+  return r;
+}
+
+// Block tile BM x BN over K steps of BK, a ring of S LDS stages, OCC blocks per
+// CU, WM x WN waves (each owns a (BM/WM) x (BN/WN) piece of the tile).
+template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
+                                                                      const int32_t* __restrict__ offsets,
+                                                                      const bf16_bits* __restrict__ B,
+                                                                      bf16_bits* __restrict__ C,
+                                                                      float* __restrict__ partials, int64_t R, int K,
+                                                                      int N, int E, int n_tiles, int min_steps) {
+  constexpr int NW = WM * WN;                  // waves
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
   constexpr int KS = BK / 16;                  // MFMA K sub-steps per stage
   constexpr int A_ROW = BK * 2;                // bytes per A row of a stage
@@ -209,8 +262,13 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
   // A: 16 consecutive rows are read together and span 16 * A_ROW bytes; the
   // chunk swizzle makes them cover the 64 banks (256 bytes) exactly once
   constexpr int A_RPP = 256 / A_ROW;           // rows per 256-byte bank period
-  static_assert(A_LD >= 1 && B_LD >= 1 && KS >= 2 && S >= 2, "unsupported tile");
+  static_assert(A_LD >= 1 && B_LD >= 1 && KS >= 2 && S >= 2 && B_SLOTS >= 16, "unsupported tile");
+  static_assert(A_LD * 1024 * NW == A_STAGE && B_LD * 1024 * NW == B_STAGE && TM >= 1 && TN >= 1, "unsupported tile");
   static_assert(A_RPP * A_CH == 16, "A swizzle assumes 16 chunks per bank period");
+  // epilogue staging: per wave WTM rows of WTN bf16
+  constexpr int EP_ROW = WTN * 2, EP_CH = WTN / 8, EP_WAVE = WTM * EP_ROW;
+  constexpr int EP_ITERS = WTM * EP_ROW / (16 * kWave);
+  static_assert(NW * EP_WAVE <= S * STAGE && EP_ITERS * 16 * kWave == WTM * EP_ROW, "epilogue staging");
 
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   __shared__ int s_tstart[257];
@@ -224,10 +282,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
   // contiguous share of the tile list for this block's XCD
   const int xcd = blockIdx.x % 8, nb = gridDim.x / 8, j = blockIdx.x / 8;
   const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+  const int nk = K / BK;
+  // whole tiles for `full` rounds, then the K steps of the `rem` leftover tiles
+  // split evenly over the XCD's blocks (stream-K)
+  const SplitK sk = split_k(hi - lo, nb, j, nk, min_steps);
 
   lds_char* const lds = (lds_char*)smem;
   const uint32_t lds_base = lds_addr(smem);
-  const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+  const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
 
   // per-lane LDS read offsets (bytes, within a stage)
   int a_rd[TM];
@@ -248,14 +310,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
   for (int ni = 0; ni < TN; ++ni) {
     const int col = wn0 + ni * 32 + (g & 1) * 16 + (q & 3) * 4;
     const int kr = q >> 2;  // == k & 3 for every k this lane reads
-    b_rd[ni] = A_STAGE + ((g >> 1) * 8 + kr) * B_ROW + (((col >> 3) ^ (2 * kr)) << 4) + (col & 7) * 2;
+    b_rd[ni] = A_STAGE + ((g >> 1) * 8 + kr) * B_ROW + (((col >> 3) ^ (4 * kr)) << 4) + (col & 7) * 2;
   }
 
-  // ---- per-tile state: tile coordinates, buffer descriptors, per-lane load offsets
+  // ---- per-item state: tile coordinates, buffer descriptors, K range, partial slot
   struct Tile {
     int e, n0;
     int64_t row0, row_end;
     i32x4 rsA, rsB;
+    int kb, kn, slot;  // first K step, K steps, partial-sum slot (-1: the item completes the tile)
   };
   auto locate = [&](int t) {
     // expert e with tstart[e] <= t < tstart[e+1] (upper bound - 1)
@@ -276,6 +339,19 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
     // descriptor's range and read as zero. B: the expert's [K, N] slab.
     tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)((tl.row_end - tl.row0) * K * 2));
     tl.rsB = buffer_rsrc(B + (int64_t)tl.e * K * N, (uint32_t)((int64_t)K * N * 2));
+    tl.kb = 0;
+    tl.kn = nk;
+    tl.slot = -1;
+    return tl;
+  };
+  auto make_item = [&](int i) {
+    if (i < sk.full) return locate(lo + j + i * nb);
+    const int r = sk.r_first + (i - sk.full);
+    Tile tl = locate(lo + sk.full * nb + r);
+    const int64_t a0 = max(sk.s0, (int64_t)r * nk), b0 = min(sk.s1, (int64_t)(r + 1) * nk);
+    tl.kb = (int)(a0 - (int64_t)r * nk);
+    tl.kn = (int)(b0 - a0);
+    tl.slot = tl.kn == nk ? -1 : (int)blockIdx.x * 2 + (i - sk.full);
     return tl;
   };
   // per-lane byte offsets of the direct-to-LDS loads (A part does not depend on the tile)
@@ -290,7 +366,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int p = (wave * B_LD + i) * 64 + lane;
-    const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (2 * (k & 3));
+    const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (4 * (k & 3));
     b_off0[i] = (uint32_t)(k * N + c * 8) * 2u;
   }
 
@@ -331,25 +407,24 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
   };
 
-  const int nk = K / BK;
   constexpr int NM = TM * TN;  // MFMAs per sub-step
   constexpr int H = NM / 2;    // MFMAs of the last sub-step before the step's barrier
   // fragment reads issued after each MFMA: a set's reads all go out in the first
   // half of the sub-step, so they have landed when the next sub-step starts
   constexpr int RPM = (NR + NM / 2 - 1) / (NM / 2);
 
-  int t = lo + j;
   Tile tl;
-  if (t < hi) {
-    tl = locate(t);
+  if (sk.n_items > 0) {
+    tl = make_item(0);
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2)
-      if (s2 < nk)
+      if (s2 < tl.kn)
 #pragma unroll
-        for (int i = 0; i < NL; ++i) issue_one(tl, s2, s2, i);
+        for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);
   }
 
-  for (; t < hi; t += nb) {
+  for (int item = 0; item < sk.n_items; ++item) {
+    const int kn = tl.kn;
     // ---- stages 0 .. S-1 of this tile were issued; wait for all of them (and older stores)
     wait_vmem<0>();
     __syncthreads();
@@ -363,7 +438,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
     int buf = 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < kn; ++kt) {
       // sub-steps 0 .. KS-2: MFMAs of the current fragments, one LDS read of the next set after each
 #pragma unroll
       for (int ks = 0; ks < KS - 1; ++ks) {
@@ -385,17 +460,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
         mfma_one(LAST, i);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool more = kt + 1 < nk;
+      const bool more = kt + 1 < kn;
       const int nbuf = buf + 1 == S ? 0 : buf + 1;
       if (more) {
         // stage kt+1 must have landed; stages kt+2 .. kt+S-1 may still be in flight
-        if (kt + S - 1 < nk)
+        if (kt + S - 1 < kn)
           wait_vmem<NL * (S - 2)>();
         else
           wait_vmem<0>();
         __syncthreads();  // every wave's stage kt+1 is in; every wave is done reading `buf`
       }
-      const bool refill = kt + S < nk;
+      const bool refill = kt + S < kn;
 #pragma unroll
       for (int i = 0; i < NM - H; ++i) {
         mfma_one(LAST, H + i);
@@ -407,7 +482,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
           if (op < NR) {
             if (more) read_one(nbuf, 0, 0, op);
           } else if (op < NR + NL) {
-            if (refill) issue_one(tl, kt + S, buf, op - NR);
+            if (refill) issue_one(tl, tl.kb + kt + S, buf, op - NR);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -416,41 +491,179 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(const bf16_bits* __
     }
     __syncthreads();  // every wave is done with every buffer
 
-    // ---- the next tile's first stages go out before this tile's epilogue
-    const Tile cur = tl;
-    if (t + nb < hi) {
-      tl = locate(t + nb);
+    if (tl.slot >= 0) {
+      // ---- part of a split tile: float32 partial sums in the accumulator
+      // layout (thread-major per MFMA register group, 16 bytes per lane)
+      float* const dst = partials + (int64_t)tl.slot * (BM * BN);
 #pragma unroll
-      for (int s2 = 0; s2 < S; ++s2)
-        if (s2 < nk)
+      for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-          for (int i = 0; i < NL; ++i) issue_one(tl, s2, s2, i);
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            f32x4 v;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mi][ni][4 * gq + qq];
+            *(f32x4*)(dst + ((int64_t)((mi * TN + ni) * 4 + gq) * (NW * kWave) + tid) * 4) = v;
+          }
+    } else {
+      // ---- epilogue through LDS: each wave stages its WTM x WTN piece as bf16 in
+      // its own region of the ring (row-major, 16-byte chunks XOR-swizzled by the
+      // row), then writes whole row segments to C with 16 bytes per lane.
+      lds_char* const ep = lds + wave * EP_WAVE;
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            // lane holds row (lane & 31) of MFMA tile (mi, ni), columns 8 gq + 4 (lane >> 5) + 0..3
+            float v[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              v[qq] = acc[mi][ni][4 * gq + qq];
+              if (GELU) v[qq] = gelu_tanh(v[qq]);
+            }
+            u32x2 o;
+            o[0] = pack_bf16x2(v[0], v[1]);
+            o[1] = pack_bf16x2(v[2], v[3]);
+            const int row = mi * 32 + (lane & 31), ch = ni * 4 + gq;
+            *(__attribute__((address_space(3))) u32x2*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4) +
+                                                          (lane >> 5) * 8) = o;
+            __builtin_amdgcn_sched_barrier(0);  // bounds the live values of the GELU pass
+          }
+      // LDS operations of one wave complete in order: no barrier between the
+      // wave's own writes and reads
+      constexpr int EP_G = EP_ITERS < 4 ? EP_ITERS : 4;  // reads in flight per group
+#pragma unroll
+      for (int it0 = 0; it0 < EP_ITERS; it0 += EP_G) {
+        u32x4 v[EP_G];
+#pragma unroll
+        for (int u = 0; u < EP_G; ++u) {
+          const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
+          v[u] = *(__attribute__((address_space(3))) u32x4*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4));
+        }
+#pragma unroll
+        for (int u = 0; u < EP_G; ++u) {
+          const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
+          const int64_t grow = tl.row0 + wm0 + row;
+          const int n = tl.n0 + wn0 + ch * 8;
+          if (grow < tl.row_end && n < N) *(u32x4*)(C + grow * N + n) = v[u];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
-    // ---- epilogue: lane holds row (lane & 31) of each MFMA tile, columns 8g + 4*(lane>>5) + 0..3
+    // ---- the next item's first stages (the ring is free once every wave has read its piece)
+    if (item + 1 < sk.n_items) {
+      __syncthreads();
+      tl = make_item(item + 1);
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-      const int64_t row = cur.row0 + wm0 + mi * 32 + (lane & 31);
-      if (row >= cur.row_end) continue;
-      bf16_bits* crow = C + row * N;
+      for (int s2 = 0; s2 < S; ++s2)
+        if (s2 < tl.kn)
 #pragma unroll
-      for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = cur.n0 + wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5);
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            v[qq] = acc[mi][ni][4 * gq + qq];
-            if (GELU) v[qq] = gelu_tanh(v[qq]);
-          }
-          u32x2 o;
-          o[0] = pack_bf16x2(v[0], v[1]);
-          o[1] = pack_bf16x2(v[2], v[3]);
-          *(u32x2*)(crow + n) = o;
-        }
+          for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);
     }
+  }
+}
+
+// Completion of the tiles that the stream-K phase split: block (b, x, r) takes
+// part b of SUB of leftover tile r of XCD x's tile range, sums the partial
+// slots of the blocks that worked on it in K order (deterministic), applies
+// the activation, rounds to bf16 and stores. Slots and the split follow the
+// GEMM kernel's own arithmetic (split_k, block index j * 8 + x).
+template <int BM, int BN, int WM, int WN, int SUB, bool GELU>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restrict__ offsets,
+                                                         const float* __restrict__ partials,
+                                                         bf16_bits* __restrict__ C, int64_t R, int nk, int N,
+                                                         int E, int n_tiles, int nb, int min_steps) {
+  constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
+  constexpr int ENT = BM * BN / 4;           // float32x4 entries per slot
+  constexpr int PER = ENT / SUB / 256;       // entries per thread
+  static_assert(PER * SUB * 256 == ENT, "fixup split");
+  constexpr int kMaxSlots = 64;  // >= blocks per XCD of any launch (kMaxCUs / 8 * 2)
+  __shared__ int s_tstart[257];
+  __shared__ int s_mtiles[256];
+  __shared__ int s_slots[kMaxSlots];
+  __shared__ int s_nslots;
+
+  const int b = blockIdx.x % SUB, x = (blockIdx.x / SUB) % 8, r = blockIdx.x / SUB / 8;
+  build_tile_list<BM>(offsets, E, R, n_tiles, s_tstart, s_mtiles);
+  const int total = s_tstart[E];
+  const int lo = (int)((int64_t)total * x / 8), hi = (int)((int64_t)total * (x + 1) / 8);
+  const int full = (hi - lo) / nb, rem = (hi - lo) - full * nb;
+  if (r >= rem || !split_leftover(rem, nb, nk, min_steps)) return;
+  const int64_t W = (int64_t)rem * nk, u0 = (int64_t)r * nk, u1 = u0 + nk;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int jj = 0; jj < nb; ++jj) {
+      const int64_t s0 = W * jj / nb, s1 = W * (jj + 1) / nb;
+      if (s0 >= u1) break;
+      if (s1 <= u0 || s1 <= s0) continue;
+      if (s0 <= u0 && s1 >= u1) {  // one block ran the whole tile and stored it
+        n = -1;
+        break;
+      }
+      if (n < kMaxSlots) s_slots[n] = (jj * 8 + x) * 2 + (r - (int)(s0 / nk));
+      ++n;
+    }
+    s_nslots = n;
+  }
+  __syncthreads();
+  const int ns = s_nslots;
+  if (ns <= 0) return;
+
+  // the tile: same enumeration as the GEMM kernel
+  const int t = lo + full * nb + r;
+  int a0 = 0, a1 = E;
+  while (a1 - a0 > 1) {
+    const int mid = (a0 + a1) >> 1;
+    if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
+  }
+  const int e = a0, local = t - s_tstart[e], mt = s_mtiles[e];
+  const int n_tile = local / mt, m_idx = local - n_tile * mt;
+  const int64_t row0 = (int64_t)offsets[e] + (int64_t)m_idx * BM;
+  const int64_t row_end = min((int64_t)offsets[e + 1], R);
+  const int n0 = n_tile * BN;
+
+  f32x4 acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ebase = b * (ENT / SUB) + threadIdx.x;
+  // slots in K order, four at a time so that their loads are in flight together
+  for (int si = 0; si < ns; si += 4) {
+    f32x4 v[4][PER];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int sl = si + q4 < ns ? s_slots[si + q4] : -1;
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        v[q4][u] = sl >= 0 ? ((const f32x4*)(partials + (int64_t)sl * (BM * BN)))[ebase + u * 256]
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
+    const int en = ebase + u * 256, grp = en / (NW * kWave), tt = en % (NW * kWave);
+    const int mi = grp / (TN * 4), ni = (grp / 4) % TN, gq = grp % 4;
+    const int wave = tt / kWave, lane = tt % kWave;
+    const int row = (wave / WN) * WTM + mi * 32 + (lane & 31);
+    const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
+    const int64_t grow = row0 + row;
+    const int n = n0 + col;
+    if (grow >= row_end || n >= N) continue;
+    float v[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];
+    u32x2 o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    *(u32x2*)(C + grow * N + n) = o;
   }
 }
 
@@ -514,6 +727,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- host side
 
+// persistent grids are sized for at most this many CUs (MI355X has 256); with two
+// blocks per CU an XCD holds at most 64 blocks, which bounds the blocks that
+// can share one split tile (gemm_fixup_kernel's slot list)
+constexpr int kMaxCUs = 256;
+
 int device_cus() {
   static int cus = 0;
   if (!cus) {
@@ -521,58 +739,109 @@ int device_cus() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
+    cus = min(max(cus, 8), kMaxCUs);
   }
   return cus;
 }
 
-// Tile configurations of the bf16 path.
-//   0: 256 x 256, K step 64, 2 stages (128 KB LDS), one block per CU
-//   1: 256 x 128, K step 32, 3 stages (72 KB LDS), two blocks per CU
-//   2: 128 x 128, K step 64, 2 stages (64 KB LDS), two blocks per CU
+// Tile configurations of the bf16 path: block tile, K step, LDS ring stages,
+// blocks per CU. LDS per block = stages * (BM + BN) * BK * 2 bytes.
 struct TileShape {
-  int bm, bn, occ;
+  const char* name;
+  int bm, bn, bk, stages, occ;
 };
-constexpr TileShape kShapes[3] = {{256, 256, 1}, {256, 128, 2}, {128, 128, 2}};
+constexpr TileShape kShapes[] = {
+    {"256x256", 256, 256, 64, 2, 1},     // 128 KB
+    {"256x256k32", 256, 256, 32, 4, 1},  // 128 KB
+    {"256x128", 256, 128, 32, 3, 2},     // 72 KB
+    {"128x128", 128, 128, 64, 2, 2},     // 64 KB
+    {"128x128k32", 128, 128, 32, 4, 2},  // 64 KB
+    {"256x256w8", 256, 256, 64, 2, 1},   // 128 KB, 8 waves
+    {"256x256w8k32", 256, 256, 32, 4, 1},  // 128 KB, 8 waves
+};
+constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
-template <int BM, int BN, int BK, int S, int OCC>
-hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, int64_t R, int K, int N,
-                       int E, bool gelu, hipStream_t s) {
+// persistent grid: OCC blocks per CU, a multiple of 8 so every XCD holds the
+// same number of blocks. MOE_GEMM_MAX_BLOCKS=<n> lowers the cap (several
+// rounds of tiles on small problems: exercises the leftover-tile split).
+int64_t persistent_grid(int64_t tiles_ub, int occ) {
+  int64_t slots = (int64_t)device_cus() / 8 * 8 * occ;
+  const char* cap = getenv("MOE_GEMM_MAX_BLOCKS");
+  if (cap && cap[0]) slots = min(slots, max((int64_t)8, (int64_t)atoi(cap) / 8 * 8));
+  return max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, slots));
+}
+
+int64_t tiles_upper_bound(int64_t R, int N, int E, int bm, int bn) {
+  const int64_t m_tiles = (R + (int64_t)E * (bm - 1)) / bm;  // >= sum over experts of ceil(rows_e / bm)
+  return m_tiles * ceil_div(N, bn);
+}
+
+constexpr int kFixupSub = 8;  // fixup blocks per split tile
+
+template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2>
+hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
+                       int K, int N, int E, bool gelu, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
-  const int64_t m_tiles = (R + (int64_t)E * (BM - 1)) / BM;  // >= sum over experts of ceil(rows_e / BM)
-  const int64_t tiles_ub = m_tiles * n_tiles;
-  if (tiles_ub > INT32_MAX) return hipErrorInvalidValue;
-  // persistent grid: OCC blocks per CU, a multiple of 8 so every XCD holds the same number of blocks
-  const int64_t slots = (int64_t)device_cus() / 8 * 8 * OCC;
-  const int64_t grid = max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, slots));
-  if (gelu)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, true>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, false>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, R, K, N, E, n_tiles);
+  const int64_t tiles_ub = tiles_upper_bound(R, N, E, BM, BN);
+  if (tiles_ub > INT32_MAX || K % BK != 0) return hipErrorInvalidValue;
+  const int64_t grid = persistent_grid(tiles_ub, OCC);
+  const int nb = (int)(grid / 8);
+  const int nk = K / BK;
+  // MOE_GEMM_SPLIT_MIN_STEPS=<n> overrides the split threshold (0: split every small leftover)
+  int min_steps = kSplitMinSteps;
+  const char* ms = getenv("MOE_GEMM_SPLIT_MIN_STEPS");
+  if (ms && ms[0]) min_steps = max(0, atoi(ms));
+  // split leftover tiles number at most nb / 3 per XCD, and none when K is short (split_leftover)
+  const unsigned fix_grid = nk >= min_steps ? (unsigned)(8 * (nb / 3) * kFixupSub) : 0u;
+  constexpr int NT = WM * WN * 64;
+  if (gelu) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
+                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
+                       n_tiles, min_steps);
+    if (fix_grid)
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
+                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
+                       n_tiles, min_steps);
+    if (fix_grid)
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+  }
   return hipGetLastError();
 }
 
 // Block tile for a GEMM: fewer, larger tiles use the matrix cores better, but
-// a last partial round of tiles over the block slots and padding rows of
-// half-empty M tiles cost time. MOE_GEMM_TILE=256x256|256x128|128x128 forces a shape.
-int pick_tile(int64_t R, int N, int E) {
+// padding rows of half-empty M tiles and a last partial round of tiles over
+// the block slots cost time (unless that round is split over the blocks, see
+// split_leftover). tile_eff: measured matrix-core efficiency of a busy CU,
+// relative to the 8-wave 256 x 256 tile; 0 = only on request.
+// MOE_GEMM_TILE=<name of a kShapes entry> forces a shape.
+int pick_tile(int64_t R, int K, int N, int E) {
   const char* force = getenv("MOE_GEMM_TILE");
-  if (force && force[0]) {
-    if (!strcmp(force, "256x256")) return 0;
-    if (!strcmp(force, "256x128")) return 1;
-    if (!strcmp(force, "128x128")) return 2;
-  }
-  const double tile_eff[3] = {0.9, 1.0, 0.8};  // relative matrix-core efficiency of a busy CU
+  if (force && force[0])
+    for (int c = 0; c < kNumShapes; ++c)
+      if (!strcmp(force, kShapes[c].name)) return c;
+  const double tile_eff[kNumShapes] = {0.0, 0.0, 0.8, 0.75, 0.0, 1.0, 0.0};
   const double cus = device_cus();
-  int best = 0;
+  int best = 5;
   double best_score = -1.0;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < kNumShapes; ++c) {
     const TileShape& ts = kShapes[c];
+    if (tile_eff[c] <= 0.0 || K % ts.bk != 0) continue;
     const double m_tiles = (double)R / ts.bm + 0.5 * E;
     const double tiles = m_tiles * ceil_div(N, ts.bn);
     const double rounds = tiles / (cus * ts.occ);
-    const double round_eff = rounds / (double)(int64_t)(rounds + 0.999);
+    const double whole = (double)(int64_t)rounds, frac = rounds - whole;
+    const int nk = K / ts.bk;
+    double round_eff;
+    if (rounds < 1.0)
+      round_eff = rounds;
+    else if (frac * 3.0 <= 1.0 && nk * (1.0 - frac) >= kSplitMinSteps)
+      round_eff = rounds / (rounds + 0.1);  // leftover split over the blocks
+    else
+      round_eff = rounds / (frac > 0.0 ? whole + 1.0 : whole);
     const double pad_eff = (double)R / (m_tiles * ts.bm);
     const double score = tile_eff[c] * round_eff * pad_eff;
     if (score > best_score) {
@@ -585,8 +854,15 @@ int pick_tile(int64_t R, int N, int E) {
 
 }  // namespace
 
+size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
+  if (dtype != MOE_DTYPE_BF16) return 0;
+  const TileShape& ts = kShapes[pick_tile(R, K, N, E)];
+  const int64_t grid = persistent_grid(tiles_upper_bound(R, N, E, ts.bm, ts.bn), ts.occ);
+  return (size_t)grid * 2 * ts.bm * ts.bn * sizeof(float);  // two split segments per block at most
+}
+
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               int64_t R, int K, int N, int E, bool gelu, hipStream_t s) {
+                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s) {
   if (dtype == MOE_DTYPE_F32) {
     const int n_tiles = (int)ceil_div(N, F_BN);
     const int64_t m_tiles = (R + (int64_t)E * (F_BM - 1)) / F_BM;
@@ -600,13 +876,21 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
                          offsets, (const float*)B, (float*)C, R, K, N, E, n_tiles, (int)grid_tiles);
     return hipGetLastError();
   }
-  switch (pick_tile(R, N, E)) {
+  switch (pick_tile(R, K, N, E)) {
     case 0:
-      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
     case 1:
-      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+    case 2:
+      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+    case 3:
+      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+    case 4:
+      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+    case 5:
+      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
     default:
-      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
   }
 }
 

@@ -27,9 +27,13 @@ hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* i
                          hipStream_t s);
 
 // C[r] = act(A[r] B[e]) for rows r of every expert group e (offsets[E+1]).
-// A [R, K], B [E, K, N], C [R, N]; act = GELU_tanh or identity.
+// A [R, K], B [E, K, N], C [R, N]; act = GELU_tanh or identity. `partials` is
+// workspace of grouped_gemm_partials_bytes() for split tiles (bf16 path).
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               int64_t R, int K, int N, int E, bool gelu, hipStream_t s);
+                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s);
+
+// Host-only bound of the partial-sum workspace one launch_grouped_gemm call may use.
+size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv,
                           const float* gate, void* y, hipStream_t s);

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -53,15 +55,27 @@ PermuteWs carve_permute(Carver& c, const moe_problem_t& p) {
   return w;
 }
 
-void* carve_ffn(Carver& c, const moe_problem_t& p) {
-  return c.take<char>((size_t)p.T * p.k * p.d_expert * elem_size(p.dtype));
+struct FfnWs {
+  void* h;           // hidden activations [T*k, d_expert]
+  float* partials;   // split-tile partial sums of either GEMM
+};
+
+FfnWs carve_ffn(Carver& c, const moe_problem_t& p) {
+  const int64_t R = p.T * p.k;
+  FfnWs w;
+  w.h = c.take<char>((size_t)R * p.d_expert * elem_size(p.dtype));
+  const size_t pb = std::max(moe::grouped_gemm_partials_bytes(p.dtype, R, p.d_model, p.d_expert, p.E),
+                             moe::grouped_gemm_partials_bytes(p.dtype, R, p.d_expert, p.d_model, p.E));
+  w.partials = c.take<float>(pb / sizeof(float));
+  return w;
 }
 
 struct ForwardWs {
   int32_t *idx, *counts, *offsets, *perm, *inv;
   float* gate;
   PermuteWs pw;
-  void *x_perm, *h, *y_perm;
+  FfnWs fw;
+  void *x_perm, *y_perm;
 };
 
 ForwardWs carve_forward(Carver& c, const moe_problem_t& p) {
@@ -76,7 +90,7 @@ ForwardWs carve_forward(Carver& c, const moe_problem_t& p) {
   w.inv = c.take<int32_t>(R);
   w.pw = carve_permute(c, p);
   w.x_perm = c.take<char>(R * p.d_model * es);
-  w.h = carve_ffn(c, p);
+  w.fw = carve_ffn(c, p);
   w.y_perm = c.take<char>(R * p.d_model * es);
   return w;
 }
@@ -155,14 +169,14 @@ MOE_API moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm,
     return MOE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < stage_bytes(*p, MOE_STAGE_GROUPED_FFN)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   Carver c(align_ws(ws));
-  void* h = carve_ffn(c, *p);
+  const FfnWs fw = carve_ffn(c, *p);
   hipStream_t s = (hipStream_t)stream;
   const int64_t R = p->T * p->k;
-  hipError_t e = moe::launch_grouped_gemm(p->dtype, x_perm, offsets, W1, h, R, p->d_model, p->d_expert, p->E,
-                                          true, s);
+  hipError_t e = moe::launch_grouped_gemm(p->dtype, x_perm, offsets, W1, fw.h, fw.partials, R, p->d_model,
+                                          p->d_expert, p->E, true, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(
-      moe::launch_grouped_gemm(p->dtype, h, offsets, W2, y_perm, R, p->d_expert, p->d_model, p->E, false, s));
+  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, R, p->d_expert,
+                                             p->d_model, p->E, false, s));
 }
 
 MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* inv,
@@ -194,10 +208,11 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
     e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts, w.pw.blockbase, s);
   if (e == hipSuccess) e = moe::launch_gather(*p, x, w.inv, w.x_perm, s);
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.h, R, p->d_model, p->d_expert, p->E, true, s);
+    e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model,
+                                 p->d_expert, p->E, true, s);
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, w.h, w.offsets, W2, w.y_perm, R, p->d_expert, p->d_model, p->E, false,
-                                 s);
+    e = moe::launch_grouped_gemm(p->dtype, w.fw.h, w.offsets, W2, w.y_perm, w.fw.partials, R, p->d_expert,
+                                 p->d_model, p->E, false, s);
   if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
   return hip_status(e);
 }

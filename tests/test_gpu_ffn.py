@@ -58,7 +58,7 @@ def test_grouped_ffn_against_oracle(moe, R, d, de, E, dtype, empty):
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256k32", "256x128", "128x128", "128x128k32", "256x256w8", "256x256w8k32"])
 def test_every_tile_shape(moe, tile):
     """Each bf16 block tile the launcher can choose, on ragged groups with
     empty experts and rows that are not a multiple of any tile."""
@@ -73,6 +73,30 @@ def test_every_tile_shape(moe, tile):
         y = run_ffn(moe, R, d, de, E, "bf16", x_perm, off.cuda(), W1, W2)
     finally:
         del os.environ["MOE_GEMM_TILE"]
+    ref = oracle_ffn("bf16", x_perm, off, W1, W2)
+    assert rel_err(f64(y), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("blocks", [24, 64])
+@pytest.mark.parametrize("tile", ["256x256w8", "128x128", "256x128"])
+@pytest.mark.parametrize("R,d,de,E", [(20000, 128, 64, 3), (9000, 512, 64, 2), (6000, 256, 192, 7)])
+def test_split_leftover_tiles(moe, tile, R, d, de, E, blocks):
+    """A capped persistent grid gives several rounds of tiles and a small
+    leftover, whose K steps are split over the blocks: tiles summed from
+    several blocks' partial sums, and (K of one or two steps) shares that are a
+    whole tile, stored by the block itself and skipped by the fixup."""
+    announce(f"ffn split tiles {tile} blocks={blocks} R={R} d={d} de={de} E={E}")
+    x_perm = make_dense((R, d), 1.0, seed=9, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=9, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=9, tag=3, device="cuda")
+    off = make_group_offsets(E, R, seed=9)
+    env = {"MOE_GEMM_TILE": tile, "MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_SPLIT_MIN_STEPS": "0"}
+    os.environ.update(env)
+    try:
+        y = run_ffn(moe, R, d, de, E, "bf16", x_perm, off.cuda(), W1, W2)
+    finally:
+        for k in env:
+            del os.environ[k]
     ref = oracle_ffn("bf16", x_perm, off, W1, W2)
     assert rel_err(f64(y), ref) <= TOL_BF16
 
