@@ -11,9 +11,11 @@
 //     all experts, padded with zero columns to EP = the next multiple of 64;
 //     four waves in a 2x2 grid each own 32 tokens x EP/2 experts as 32x32
 //     MFMA tiles (v_mfma_f32_32x32x16_bf16, float32 accumulators).
-//     x tiles sit K-contiguous in LDS; w_router tiles stay E-contiguous and are
-//     read with ds_read_b64_tr_b16 (4 consecutive k of one column per lane).
-//     The float32 logits of the block land in LDS for the epilogue.
+//     Operands stream HBM -> LDS through a ring of stages with direct-to-LDS
+//     loads and one barrier per K step; x tiles sit K-contiguous in LDS,
+//     w_router tiles stay E-contiguous and are read with ds_read_b64_tr_b16
+//     (4 consecutive k of one column per lane). The float32 logits of the
+//     block land in the (then idle) ring for the epilogue.
 //   * otherwise (float32, or E not a multiple of 8): one wave per token; each
 //     lane takes 16-byte pieces of the token's row and multiplies them with
 //     the matching w_router rows for up to 8 experts at a time; per-expert
@@ -24,14 +26,11 @@
 //     the lower half, so equal logits favour the lower index).
 #include "common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace moe {
 
 namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Softmax statistics and top-k of one token whose E logits are in LDS (`lg`).
 __device__ __forceinline__ void select_topk(const float* lg, int E, int k, int64_t t, float* __restrict__ logits,
@@ -69,78 +68,148 @@ __device__ __forceinline__ void select_topk(const float* lg, int E, int k, int64
 
 // ---------------------------------------------------------------- matrix-core path
 
-constexpr int RT = 64;   // tokens per block
-constexpr int RK = 64;   // K step
+constexpr int RT = 64;  // tokens per block
+constexpr int RBK = 64; // K step
 
-// E_T: padded experts per wave column = EP / 2 (32 .. 128); E (<= EP, multiple of 8) at run time
-template <int E_T>
+// Block: RT tokens x EP experts (E padded), four waves in a 2x2 grid, each
+// 32 tokens x EP/2 experts. Operands stream HBM -> LDS through a ring of S
+// stages with direct-to-LDS loads (x rows K-contiguous, chunk XOR-swizzled;
+// w_router rows E-contiguous, read with the transposing LDS read), one
+// barrier per K step, the fragments of the next K sub-step read while the
+// MFMAs of the current one run. After the last step the ring holds the
+// block's float32 logits (+ bias) for the selection epilogue.
+template <int EP, int S>
 __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __restrict__ x,
                                                          const bf16_bits* __restrict__ wr,
                                                          const float* __restrict__ bias, float* __restrict__ logits,
                                                          int32_t* __restrict__ idx, float* __restrict__ gate,
                                                          int64_t T, int d, int E_real, int k) {
-  constexpr int E = 2 * E_T;  // padded width
-  constexpr int TN = E_T / 32;       // 32x32 tiles per wave along experts
-  constexpr int X_ROW = RK * 2;      // bytes per token row of an x tile
-  constexpr int W_ROW = E * 2;       // bytes per k row of a w tile
-  __shared__ __attribute__((aligned(16))) char xs[RT * X_ROW];
-  __shared__ __attribute__((aligned(16))) char ws[RK * W_ROW];
-  __shared__ float lg[RT][E + 1];
+  constexpr int NW = 4;
+  constexpr int WTN = EP / 2, TN = WTN / 32;  // experts per wave, 32-wide MFMA tiles
+  constexpr int KS = RBK / 16;                // MFMA K sub-steps per stage
+  constexpr int A_ROW = RBK * 2, A_STAGE = RT * A_ROW;
+  constexpr int B_ROW = EP * 2, B_SLOTS = EP / 8, B_STAGE = RBK * B_ROW;
+  constexpr int STAGE = A_STAGE + B_STAGE;
+  constexpr int A_LD = A_STAGE / 1024 / NW, B_LD = B_STAGE / 1024 / NW, NL = A_LD + B_LD;
+  constexpr int BSW = B_SLOTS >= 16 ? 4 : 2;  // B chunk swizzle: XOR by BSW * (k & 3)
+  constexpr int LG_ROW = EP + 1;              // float32 logits row in the epilogue
+  constexpr int RING = S * STAGE;
+  constexpr int SMEM = RING > RT * LG_ROW * 4 ? RING : RT * LG_ROW * 4;
+  static_assert(A_LD * 1024 * NW == A_STAGE && B_LD * 1024 * NW == B_STAGE && TN >= 1, "router tile");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t t0 = (int64_t)blockIdx.x * RT;
-  const int wm0 = (wave >> 1) * 32, wn0 = (wave & 1) * E_T;
+  const int wm0 = (wave >> 1) * 32, wn0 = (wave & 1) * WTN;
+  lds_char* const lds = (lds_char*)smem;
+  const uint32_t lds_base = lds_addr(smem);
+  const int nk = d / RBK;
 
+  // tokens past T and k past d read as zero (descriptor ranges)
+  const int rows = (int)min((int64_t)RT, T - t0);
+  const i32x4 rsA = buffer_rsrc(x + t0 * d, (uint32_t)(rows * d * 2));
+  const i32x4 rsB = buffer_rsrc(wr, (uint32_t)(d * E_real * 2));
+
+  // per-lane DMA offsets: x piece (row, chunk), w piece (k, chunk); chunks of
+  // padded experts (>= E_real) point past the range and load zeros (were the
+  // scalar K offset to wrap them back into range, they would read other w
+  // elements into columns that are never used)
+  uint32_t a_off[A_LD], b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int p = (wave * A_LD + i) * kWave + lane;
+    const int row = p / 8, c = (p % 8) ^ ((row >> 1) & 7);
+    a_off[i] = (uint32_t)(row * d + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int p = (wave * B_LD + i) * kWave + lane;
+    const int kk = p / B_SLOTS, c = (p % B_SLOTS) ^ (BSW * (kk & 3));
+    b_off[i] = c * 8 < E_real ? (uint32_t)(kk * E_real + c * 8) * 2u : 0xFFFFFFF0u;
+  }
+  auto issue_one = [&](int kt, int buf, int i) {
+    const uint32_t st = lds_base + buf * STAGE;
+    if (i < A_LD)
+      buffer_load_lds16(rsA, a_off[i], (uint32_t)kt * RBK * 2, st + (wave * A_LD + i) * 1024);
+    else
+      buffer_load_lds16(rsB, b_off[i - A_LD], (uint32_t)kt * RBK * E_real * 2,
+                        st + A_STAGE + (wave * B_LD + i - A_LD) * 1024);
+  };
+
+  // fragment read offsets
+  const int a_rd = (wm0 + (lane & 31)) * A_ROW;
+  int a_x[KS];
+  {
+    const int sw = ((lane & 31) >> 1) & 7;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a_x[ks] = ((ks * 2 + (lane >> 5)) ^ sw) << 4;
+  }
+  const int q = lane & 15, g = lane >> 4, kr = q >> 2;
+  int b_rd[TN];
+#pragma unroll
+  for (int ni = 0; ni < TN; ++ni) {
+    const int col = wn0 + ni * 32 + (g & 1) * 16 + (q & 3) * 4;
+    b_rd[ni] = A_STAGE + ((g >> 1) * 8 + kr) * B_ROW + (((col >> 3) ^ (BSW * kr)) << 4) + (col & 7) * 2;
+  }
+  bf16x8 fa[2], fb[2][TN];
+  auto read_set = [&](int buf, int ks, int set) {
+    lds_char* const st = lds + buf * STAGE;
+    fa[set] = *(lds_bf16x8*)(st + a_rd + a_x[ks]);
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+      lds_char* const p0 = st + ks * 16 * B_ROW + b_rd[ni];
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * B_ROW));
+      fb[set][ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
   f32x16 acc[TN];
 #pragma unroll
   for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[ni][v] = 0.0f;
 
-  // fragment read offsets
-  const int a_row = wm0 + (lane & 31);
-  const int q = lane & 15, g = lane >> 4, kr = q >> 2;
-  int b_rd[TN];
 #pragma unroll
-  for (int ni = 0; ni < TN; ++ni) {
-    const int col = wn0 + ni * 32 + (g & 1) * 16 + (q & 3) * 4;
-    b_rd[ni] = ((g >> 1) * 8 + kr) * W_ROW + (((col >> 3) ^ (2 * kr)) << 4) + (col & 7) * 2;
-  }
+  for (int s2 = 0; s2 < S; ++s2)
+    if (s2 < nk)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) issue_one(s2, s2, i);
+  if (nk > S - 1)
+    wait_vmem<NL * (S - 1)>();
+  else
+    wait_vmem<0>();
+  __syncthreads();
+  read_set(0, 0, 0);
 
-  for (int c0 = 0; c0 < d; c0 += RK) {
-    // x tile: 64 tokens x 64 k, 16-byte pieces, chunk XOR-ed by ((row >> 1) & 7)
-    for (int p = tid; p < RT * 8; p += 256) {
-      const int row = p >> 3, c = p & 7;
-      const int64_t t = min(t0 + row, T - 1);
-      const u32x4 v = *(const u32x4*)(x + t * d + c0 + c * 8);
-      *(u32x4*)(xs + row * X_ROW + ((c ^ ((row >> 1) & 7)) << 4)) = v;
-    }
-    // w tile: 64 k rows x EP (zero past E_real), chunk XOR-ed by 2*(k & 3)
-    for (int p = tid; p < RK * (E / 8); p += 256) {
-      const int kk = p / (E / 8), c = p % (E / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c * 8 < E_real) v = *(const u32x4*)(wr + (int64_t)(c0 + kk) * E_real + c * 8);
-      *(u32x4*)(ws + kk * W_ROW + ((c ^ (2 * (kk & 3))) << 4)) = v;
-    }
-    __syncthreads();
+  int buf = 0;
+  for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-    for (int ks = 0; ks < RK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      const bf16x8 fa = *(const bf16x8*)(xs + a_row * X_ROW + ((kc ^ ((a_row >> 1) & 7)) << 4));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int set = ks & 1;
+      if (ks + 1 < KS) read_set(buf, ks + 1, set ^ 1);
 #pragma unroll
-      for (int ni = 0; ni < TN; ++ni) {
-        const char* p0 = ws + ks * 16 * W_ROW + b_rd[ni];
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)p0);
-        const s16x4 hi4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(p0 + 4 * W_ROW));
-        const s16x8 v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), fa, acc[ni], 0, 0, 0);
-      }
+      for (int ni = 0; ni < TN; ++ni)
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set], acc[ni], 0, 0, 0);
     }
-    __syncthreads();
+    if (kt + 1 < nk) {
+      // stage kt+1 has landed once at most the loads of stages kt+2 .. kt+S-1 are outstanding
+      if (kt + S - 1 < nk)
+        wait_vmem<NL * (S - 2)>();
+      else
+        wait_vmem<0>();
+      __syncthreads();  // every wave is done with `buf`; stage kt+1 is visible
+      if (kt + S < nk)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) issue_one(kt + S, buf, i);
+      buf = buf + 1 == S ? 0 : buf + 1;
+      read_set(buf, 0, 0);
+    }
   }
+  __syncthreads();  // the ring becomes the logits buffer
 
-  // logits to LDS: lane holds token (lane & 31) of the wave's rows, experts 8g + 4*(lane>>5) + 0..3
+  // lane holds token (lane & 31) of the wave's rows, experts 8 gq + 4 (lane >> 5) + 0..3 of each tile
+  float* const lg = (float*)smem;
 #pragma unroll
   for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
@@ -148,12 +217,12 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int e = wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5) + qq;
-        if (e < E_real) lg[wm0 + (lane & 31)][e] = acc[ni][4 * gq + qq] + (bias ? bias[e] : 0.0f);
+        if (e < E_real) lg[(wm0 + (lane & 31)) * LG_ROW + e] = acc[ni][4 * gq + qq] + (bias ? bias[e] : 0.0f);
       }
   __syncthreads();
-  for (int r = wave; r < RT; r += 4) {
+  for (int r = wave; r < RT; r += NW) {
     const int64_t t = t0 + r;
-    if (t < T) select_topk(lg[r], E_real, k, t, logits, idx, gate);
+    if (t < T) select_topk(lg + r * LG_ROW, E_real, k, t, logits, idx, gate);
   }
 }
 
@@ -250,15 +319,16 @@ hipError_t launch_route(const moe_problem_t& p, const void* x, const void* w_rou
                          p.d_model, p.E, p.k);
       return hipGetLastError();
     };
+    // ring stages: 4 while a stage is small, 3 for the widest tiles (LDS: S * (8 KB + 128 * EP B))
     switch (ep) {
       case 64:
-        return go(route_mfma_kernel<32>);
+        return go(route_mfma_kernel<64, 4>);
       case 128:
-        return go(route_mfma_kernel<64>);
+        return go(route_mfma_kernel<128, 4>);
       case 192:
-        return go(route_mfma_kernel<96>);
+        return go(route_mfma_kernel<192, 3>);
       default:
-        return go(route_mfma_kernel<128>);
+        return go(route_mfma_kernel<256, 3>);
     }
   }
   const int64_t blocks = ceil_div(p.T, kRouteWaves);
