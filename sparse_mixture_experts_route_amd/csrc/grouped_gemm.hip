@@ -368,16 +368,27 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   if (sk.n_items > 0) {
     tl = make_item(0);
 #pragma unroll
-    for (int s2 = 0; s2 < S; ++s2)
+    for (int s2 = 0; s2 < (S >= 3 ? S - 1 : S); ++s2)
       if (s2 < tl.kn)
 #pragma unroll
         for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);
   }
 
+  // With three or more stages the refill of a buffer is spread over all the
+  // MFMAs of a K step (a direct-to-LDS load stalls the issuing wave, and the
+  // waves leave each barrier together: a burst of loads right after it idles
+  // the matrix cores). Step kt then loads stage kt+S-1 into the buffer that
+  // step kt-1 freed, and an item's prologue issues stages 0 .. S-2.
+  constexpr bool SPREAD = S >= 3;
+  constexpr int PRO = SPREAD ? S - 1 : S;  // stages issued by an item's prologue
+
   for (int item = 0; item < sk.n_items; ++item) {
     const int kn = tl.kn;
-    // ---- stages 0 .. S-1 of this tile were issued; wait for all of them (and older stores)
-    wait_vmem<0>();
+    // ---- wait for stage 0 of this item (and everything issued before it)
+    if (kn >= PRO)
+      wait_vmem<NL * (PRO - 1)>();
+    else
+      wait_vmem<0>();
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
@@ -389,6 +400,62 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
     int buf = 0;
+    if constexpr (SPREAD) {
+      constexpr int STEP_M = KS * NM;            // MFMAs per K step
+      constexpr int BAR_M = (KS - 1) * NM + H;   // MFMAs before the step's barrier
+      // refill load d goes out after MFMA (d * STEP_M) / NL of the step; NB of them precede the barrier
+      constexpr int NB = (BAR_M * NL + STEP_M - 1) / STEP_M;
+      constexpr int LAST = (KS - 1) & 1;
+      for (int kt = 0; kt < kn; ++kt) {
+        const bool refill = kt + S - 1 < kn;
+        const int rbuf = buf == 0 ? S - 1 : buf - 1;  // freed by step kt-1
+        auto dma_after = [&](int m) {
+#pragma unroll
+          for (int d = 0; d < NL; ++d)
+            if ((d * STEP_M) / NL == m && refill) issue_one(tl, tl.kb + kt + S - 1, rbuf, d);
+        };
+#pragma unroll
+        for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+          for (int i = 0; i < NM; ++i) {
+            mfma_one(ks & 1, i);
+#pragma unroll
+            for (int u = 0; u < RPM; ++u)
+              if (i * RPM + u < NR) read_one(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
+            dma_after(ks * NM + i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          mfma_one(LAST, i);
+          dma_after((KS - 1) * NM + i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const bool more = kt + 1 < kn;
+        const int nbuf = buf + 1 == S ? 0 : buf + 1;
+        if (more) {
+          // stage kt+1 must have landed: still in flight may be stages kt+2 .. kt+S-2
+          // and the NB loads of stage kt+S-1 issued so far
+          if (refill)
+            wait_vmem<NL * (S - 3) + NB>();
+          else
+            wait_vmem<0>();
+          __syncthreads();  // stage kt+1 is visible; every wave is done reading `buf`
+        }
+        constexpr int PER = (NR + (NM - H) - 1) / (NM - H);  // next-stage fragment reads per MFMA
+#pragma unroll
+        for (int i = 0; i < NM - H; ++i) {
+          mfma_one(LAST, H + i);
+#pragma unroll
+          for (int u = 0; u < PER; ++u)
+            if (i * PER + u < NR && more) read_one(nbuf, 0, 0, i * PER + u);
+          dma_after((KS - 1) * NM + H + i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        buf = nbuf;
+      }
+    } else {
     for (int kt = 0; kt < kn; ++kt) {
       // sub-steps 0 .. KS-2: MFMAs of the current fragments, one LDS read of the next set after each
 #pragma unroll
@@ -439,6 +506,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
         __builtin_amdgcn_sched_barrier(0);
       }
       buf = nbuf;
+    }
     }
     __syncthreads();  // every wave is done with every buffer
 
@@ -510,7 +578,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
       __syncthreads();
       tl = make_item(item + 1);
 #pragma unroll
-      for (int s2 = 0; s2 < S; ++s2)
+      for (int s2 = 0; s2 < PRO; ++s2)
         if (s2 < tl.kn)
 #pragma unroll
           for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);

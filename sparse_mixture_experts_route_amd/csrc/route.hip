@@ -66,6 +66,70 @@ __device__ __forceinline__ void select_topk(const float* lg, int E, int k, int64
   }
 }
 
+// Top-k (k <= kTopkFast) of the RT tokens of a block whose logits are in LDS
+// (row r at lg + r * ld): four threads per token, thread q of the group scans
+// experts q, q + 4, ... keeping the kTopkFast largest 64-bit keys (the keys of
+// select_topk: order-preserving logit bits above the inverted expert index,
+// all distinct) in a sorted register list; the four lists are merged over two
+// rounds of lane exchanges, so the result equals select_topk's selection.
+// Softmax maximum and sum are combined the same way (fixed order).
+constexpr int kTopkFast = 8;
+
+__device__ __forceinline__ void insert_key(uint64_t (&top)[kTopkFast], uint64_t v) {
+#pragma unroll
+  for (int j = 0; j < kTopkFast; ++j) {
+    const uint64_t hi = top[j] > v ? top[j] : v;
+    v = top[j] > v ? v : top[j];
+    top[j] = hi;
+  }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int RT_>
+__device__ __forceinline__ void select_topk_block(const float* lg, int ld, int64_t t0, int64_t T, int E, int k,
+                                                  int32_t* __restrict__ idx, float* __restrict__ gate) {
+  static_assert(RT_ * 4 == 256, "four threads per token, 256 threads");
+  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const float* row = lg + r * ld;
+  uint64_t top[kTopkFast];
+#pragma unroll
+  for (int j = 0; j < kTopkFast; ++j) top[j] = 0;  // below every finite logit's key
+  float m = -INFINITY;
+  for (int e = q; e < E; e += 4) {
+    const float l = row[e];
+    m = fmaxf(m, l);
+    insert_key(top, ((uint64_t)float_order_key(l) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, kWave));
+  m = fmaxf(m, __shfl_xor(m, 2, kWave));
+  float ssum = 0.0f;
+  for (int e = q; e < E; e += 4) ssum += expf(row[e] - m);
+  ssum += __shfl_xor(ssum, 1, kWave);
+  ssum += __shfl_xor(ssum, 2, kWave);
+#pragma unroll
+  for (int o = 1; o <= 2; o <<= 1) {
+    uint64_t other[kTopkFast];
+#pragma unroll
+    for (int j = 0; j < kTopkFast; ++j) other[j] = shfl_xor_u64(top[j], o);
+#pragma unroll
+    for (int j = 0; j < kTopkFast; ++j) insert_key(top, other[j]);
+  }
+  const int64_t t = t0 + r;
+  if (q == 0 && t < T) {
+#pragma unroll
+    for (int j = 0; j < kTopkFast; ++j)
+      if (j < k) {
+        const int es = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
+        idx[t * k + j] = es;
+        gate[t * k + j] = expf(row[es] - m) / ssum;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- matrix-core path
 
 constexpr int RT = 64;  // tokens per block
@@ -220,9 +284,18 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
         if (e < E_real) lg[(wm0 + (lane & 31)) * LG_ROW + e] = acc[ni][4 * gq + qq] + (bias ? bias[e] : 0.0f);
       }
   __syncthreads();
-  for (int r = wave; r < RT; r += NW) {
-    const int64_t t = t0 + r;
-    if (t < T) select_topk(lg + r * LG_ROW, E_real, k, t, logits, idx, gate);
+  if (k <= kTopkFast) {
+    select_topk_block<RT>(lg, LG_ROW, t0, T, E_real, k, idx, gate);
+    if (logits)  // rows of the block, coalesced
+      for (int i = tid; i < RT * E_real; i += NW * kWave) {
+        const int r = i / E_real, e = i - r * E_real;
+        if (t0 + r < T) logits[(t0 + r) * E_real + e] = lg[r * LG_ROW + e];
+      }
+  } else {
+    for (int r = wave; r < RT; r += NW) {
+      const int64_t t = t0 + r;
+      if (t < T) select_topk(lg + r * LG_ROW, E_real, k, t, logits, idx, gate);
+    }
   }
 }
 
