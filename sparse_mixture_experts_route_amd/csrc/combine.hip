@@ -23,12 +23,56 @@ __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
   }
 }
 
+constexpr int kCombineFastK = 8;  // selections per token whose rows are loaded together
+constexpr int kCombineU = 2;      // 16-byte pieces per lane per row in flight
+
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_bf16_kernel(
     const u32x4* __restrict__ y_perm, const int32_t* __restrict__ inv, const float* __restrict__ gate,
     u32x4* __restrict__ y, int64_t T, int k, int64_t row_vecs, int64_t rows) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kCombineWaves + threadIdx.x / kWave;
   if (t >= T) return;
+  if (k <= kCombineFastK) {
+    // the token's k source rows and gates, once; invalid selections contribute nothing
+    int64_t src[kCombineFastK];
+    float g[kCombineFastK];
+#pragma unroll
+    for (int j = 0; j < kCombineFastK; ++j) {
+      const int32_t r = j < k ? inv[t * k + j] : -1;
+      const bool ok = r >= 0 && r < rows;
+      src[j] = ok ? (int64_t)r * row_vecs : -1;
+      g[j] = ok ? gate[t * k + j] : 0.0f;
+    }
+    for (int64_t c0 = lane; c0 < row_vecs; c0 += kWave * kCombineU) {
+      // all loads of this step first, then the accumulation in selection order
+      u32x4 v[kCombineFastK][kCombineU];
+#pragma unroll
+      for (int j = 0; j < kCombineFastK; ++j)
+#pragma unroll
+        for (int u = 0; u < kCombineU; ++u)
+          if (src[j] >= 0 && c0 + u * kWave < row_vecs) v[j][u] = y_perm[src[j] + c0 + u * kWave];
+#pragma unroll
+      for (int u = 0; u < kCombineU; ++u) {
+        if (c0 + u * kWave >= row_vecs) continue;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kCombineFastK; ++j) {
+          if (src[j] < 0) continue;
+          float f[8];
+          unpack8(v[j][u], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
+        }
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        y[t * row_vecs + c0 + u * kWave] = o;
+      }
+    }
+    return;
+  }
   for (int64_t c = lane; c < row_vecs; c += kWave) {
     float acc[8];
 #pragma unroll

@@ -111,7 +111,12 @@ __global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict_
 // One wave per token: the row is read once in 16-byte pieces and written to
 // each of the token's k rows.
 constexpr int kGatherWaves = 4;
+constexpr int kGatherFastK = 8;  // selections per token handled with the rows held in registers
+constexpr int kGatherU = 4;      // 16-byte pieces per lane in flight per row
 
+// One wave per token: the token's row is read once, U pieces per lane at a
+// time, and written to each of its k rows of x_perm. The k destination rows
+// are read once per token.
 __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(const u32x4* __restrict__ x,
                                                                       const int32_t* __restrict__ inv,
                                                                       u32x4* __restrict__ x_perm, int64_t T,
@@ -120,6 +125,27 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(const u32x
   const int64_t t = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave;
   if (t >= T) return;
   const u32x4* src = x + t * row_vecs;
+  if (k <= kGatherFastK) {
+    int64_t dst[kGatherFastK];
+#pragma unroll
+    for (int j = 0; j < kGatherFastK; ++j) {
+      const int32_t r = j < k ? inv[t * k + j] : -1;
+      dst[j] = (r >= 0 && r < rows) ? (int64_t)r * row_vecs : -1;
+    }
+    for (int64_t c0 = lane; c0 < row_vecs; c0 += kWave * kGatherU) {
+      u32x4 v[kGatherU];
+#pragma unroll
+      for (int u = 0; u < kGatherU; ++u)
+        if (c0 + u * kWave < row_vecs) v[u] = src[c0 + u * kWave];
+#pragma unroll
+      for (int j = 0; j < kGatherFastK; ++j)
+        if (dst[j] >= 0)
+#pragma unroll
+          for (int u = 0; u < kGatherU; ++u)
+            if (c0 + u * kWave < row_vecs) x_perm[dst[j] + c0 + u * kWave] = v[u];
+    }
+    return;
+  }
   for (int64_t c = lane; c < row_vecs; c += kWave) {
     const u32x4 v = src[c];
     for (int j = 0; j < k; ++j) {
