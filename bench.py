@@ -110,7 +110,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="mixtral_coarse",
                     help="workload: tiny_fp32, mixtral_coarse, fine_grained, skewed, large_sparse")
     ap.add_argument("--seed", type=int, default=0)
@@ -148,22 +148,10 @@ def main():
     layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, x.dtype, device=dev)
     stream = torch.cuda.current_stream()
 
-    # ---- timed region A: whole-layer steps through moe_forward
-    for _ in range(args.warmup):
-        layer(x, wr, W1, W2, b)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        layer(x, wr, W1, W2, b)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # ---- timed region B: the same work through the four stage entry points,
-    # with HIP events between phases on the stream the kernels run on
+    # ---- per-phase region: the same work through the four stage entry points,
+    # with HIP events between phases on the stream the kernels run on. It runs
+    # first: the GPU's clocks take tens of milliseconds of load to settle, and
+    # the headline region below should measure the steady state
     p = layer.problem
     R = cfg.T * cfg.k
     bufs = layer.stages(x, wr, W1, W2, b, logits=False)  # allocates the stage outputs once
@@ -195,6 +183,22 @@ def main():
         stage_step(events[s])
     torch.cuda.synchronize()
     phase_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, n in enumerate(names)}
+
+    # ---- timed region: whole-layer steps through moe_forward (the headline)
+    for _ in range(args.warmup):
+        layer(x, wr, W1, W2, b)
+    torch.cuda.synchronize()
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    wall0 = time.perf_counter()
+    step_ev[0].record(stream)
+    for i in range(args.steps):
+        layer(x, wr, W1, W2, b)
+        step_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = step_ev[0].elapsed_time(step_ev[-1]) / args.steps
+    per_step = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
+
     assert torch.equal(bufs["y"], layer.y), "stage path and moe_forward disagree"
 
     flops = cfg.ffn_flops()
@@ -226,6 +230,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

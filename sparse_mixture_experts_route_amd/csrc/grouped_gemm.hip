@@ -155,6 +155,11 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
 // saves, (nb - rem) / nb of a tile, outweigh the partial-sum traffic and the
 // fixup launch, which cost about as much as `min_steps` K steps (24 measured
 // on gfx950 with 256 x 256 tiles).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 struct SplitK {
   int full, rem, r_first, n_items;
   int64_t s0, s1;
@@ -391,123 +396,140 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
       wait_vmem<0>();
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-#pragma unroll
     for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-    int buf = 0;
-    if constexpr (SPREAD) {
-      constexpr int STEP_M = KS * NM;            // MFMAs per K step
-      constexpr int BAR_M = (KS - 1) * NM + H;   // MFMAs before the step's barrier
-      // refill load d goes out after MFMA (d * STEP_M) / NL of the step; NB of them precede the barrier
-      constexpr int NB = (BAR_M * NL + STEP_M - 1) / STEP_M;
-      constexpr int LAST = (KS - 1) & 1;
-      for (int kt = 0; kt < kn; ++kt) {
-        const bool refill = kt + S - 1 < kn;
-        const int rbuf = buf == 0 ? S - 1 : buf - 1;  // freed by step kt-1
-        auto dma_after = [&](int m) {
+    // a wave whose whole slab of rows lies past the expert group's end (the
+    // last, partly filled M tile of a group) skips its fragment reads and
+    // MFMAs but still issues its share of the loads and joins the barriers;
+    // the other wave on its SIMD then has the matrix core to itself
+    auto kloop = [&](auto live_c) {
+      constexpr bool LIVE = decltype(live_c)::value;
+      auto mfma_x = [&](int set, int idx) {
+        if constexpr (LIVE) mfma_one(set, idx);
+      };
+      auto read_x = [&](int b_, int ks_, int set_, int r_) {
+        if constexpr (LIVE) read_one(b_, ks_, set_, r_);
+      };
 #pragma unroll
-          for (int d = 0; d < NL; ++d)
-            if ((d * STEP_M) / NL == m && refill) issue_one(tl, tl.kb + kt + S - 1, rbuf, d);
-        };
+      for (int r = 0; r < NR; ++r) read_x(0, 0, 0, r);
+      int buf = 0;
+      if constexpr (SPREAD) {
+        constexpr int STEP_M = KS * NM;            // MFMAs per K step
+        constexpr int BAR_M = (KS - 1) * NM + H;   // MFMAs before the step's barrier
+        // refill load d goes out after MFMA (d * STEP_M) / NL of the step; NB of them precede the barrier
+        constexpr int NB = (BAR_M * NL + STEP_M - 1) / STEP_M;
+        constexpr int LAST = (KS - 1) & 1;
+        for (int kt = 0; kt < kn; ++kt) {
+          const bool refill = kt + S - 1 < kn;
+          const int rbuf = buf == 0 ? S - 1 : buf - 1;  // freed by step kt-1
+          auto dma_after = [&](int m) {
+#pragma unroll
+            for (int d = 0; d < NL; ++d)
+              if ((d * STEP_M) / NL == m && refill) issue_one(tl, tl.kb + kt + S - 1, rbuf, d);
+          };
+#pragma unroll
+          for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+              mfma_x(ks & 1, i);
+#pragma unroll
+              for (int u = 0; u < RPM; ++u)
+                if (i * RPM + u < NR) read_x(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
+              dma_after(ks * NM + i);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < H; ++i) {
+            mfma_x(LAST, i);
+            dma_after((KS - 1) * NM + i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const bool more = kt + 1 < kn;
+          const int nbuf = buf + 1 == S ? 0 : buf + 1;
+          if (more) {
+            // stage kt+1 must have landed: still in flight may be stages kt+2 .. kt+S-2
+            // and the NB loads of stage kt+S-1 issued so far
+            if (refill)
+              wait_vmem<NL * (S - 3) + NB>();
+            else
+              wait_vmem<0>();
+            __syncthreads();  // stage kt+1 is visible; every wave is done reading `buf`
+          }
+          constexpr int PER = (NR + (NM - H) - 1) / (NM - H);  // next-stage fragment reads per MFMA
+#pragma unroll
+          for (int i = 0; i < NM - H; ++i) {
+            mfma_x(LAST, H + i);
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+              if (i * PER + u < NR && more) read_x(nbuf, 0, 0, i * PER + u);
+            dma_after((KS - 1) * NM + H + i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          buf = nbuf;
+        }
+      } else {
+      for (int kt = 0; kt < kn; ++kt) {
+        // sub-steps 0 .. KS-2: MFMAs of the current fragments, one LDS read of the next set after each
 #pragma unroll
         for (int ks = 0; ks < KS - 1; ++ks) {
 #pragma unroll
           for (int i = 0; i < NM; ++i) {
-            mfma_one(ks & 1, i);
+            mfma_x(ks & 1, i);
 #pragma unroll
             for (int u = 0; u < RPM; ++u)
-              if (i * RPM + u < NR) read_one(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
-            dma_after(ks * NM + i);
+              if (i * RPM + u < NR) read_x(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        // last sub-step: H MFMAs, the step's barrier, then the rest of the MFMAs
+        // with the refill of this buffer (stage kt+S) and the next stage's first
+        // fragment reads spread between them
+        constexpr int LAST = (KS - 1) & 1;
 #pragma unroll
         for (int i = 0; i < H; ++i) {
-          mfma_one(LAST, i);
-          dma_after((KS - 1) * NM + i);
+          mfma_x(LAST, i);
           __builtin_amdgcn_sched_barrier(0);
         }
         const bool more = kt + 1 < kn;
         const int nbuf = buf + 1 == S ? 0 : buf + 1;
         if (more) {
-          // stage kt+1 must have landed: still in flight may be stages kt+2 .. kt+S-2
-          // and the NB loads of stage kt+S-1 issued so far
-          if (refill)
-            wait_vmem<NL * (S - 3) + NB>();
+          // stage kt+1 must have landed; stages kt+2 .. kt+S-1 may still be in flight
+          if (kt + S - 1 < kn)
+            wait_vmem<NL * (S - 2)>();
           else
             wait_vmem<0>();
-          __syncthreads();  // stage kt+1 is visible; every wave is done reading `buf`
+          __syncthreads();  // every wave's stage kt+1 is in; every wave is done reading `buf`
         }
-        constexpr int PER = (NR + (NM - H) - 1) / (NM - H);  // next-stage fragment reads per MFMA
+        const bool refill = kt + S < kn;
 #pragma unroll
         for (int i = 0; i < NM - H; ++i) {
-          mfma_one(LAST, H + i);
+          mfma_x(LAST, H + i);
+          constexpr int PER = (NL + NR + (NM - H) - 1) / (NM - H);  // memory ops per MFMA
 #pragma unroll
-          for (int u = 0; u < PER; ++u)
-            if (i * PER + u < NR && more) read_one(nbuf, 0, 0, i * PER + u);
-          dma_after((KS - 1) * NM + H + i);
+          for (int u = 0; u < PER; ++u) {
+            // the next stage's first fragments first (needed soonest), then the refill loads
+            const int op = i * PER + u;
+            if (op < NR) {
+              if (more) read_x(nbuf, 0, 0, op);
+            } else if (op < NR + NL) {
+              if (refill) issue_one(tl, tl.kb + kt + S, buf, op - NR);
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         buf = nbuf;
       }
-    } else {
-    for (int kt = 0; kt < kn; ++kt) {
-      // sub-steps 0 .. KS-2: MFMAs of the current fragments, one LDS read of the next set after each
-#pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          mfma_one(ks & 1, i);
-#pragma unroll
-          for (int u = 0; u < RPM; ++u)
-            if (i * RPM + u < NR) read_one(buf, ks + 1, (ks + 1) & 1, i * RPM + u);
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
-      // last sub-step: H MFMAs, the step's barrier, then the rest of the MFMAs
-      // with the refill of this buffer (stage kt+S) and the next stage's first
-      // fragment reads spread between them
-      constexpr int LAST = (KS - 1) & 1;
-#pragma unroll
-      for (int i = 0; i < H; ++i) {
-        mfma_one(LAST, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const bool more = kt + 1 < kn;
-      const int nbuf = buf + 1 == S ? 0 : buf + 1;
-      if (more) {
-        // stage kt+1 must have landed; stages kt+2 .. kt+S-1 may still be in flight
-        if (kt + S - 1 < kn)
-          wait_vmem<NL * (S - 2)>();
-        else
-          wait_vmem<0>();
-        __syncthreads();  // every wave's stage kt+1 is in; every wave is done reading `buf`
-      }
-      const bool refill = kt + S < kn;
-#pragma unroll
-      for (int i = 0; i < NM - H; ++i) {
-        mfma_one(LAST, H + i);
-        constexpr int PER = (NL + NR + (NM - H) - 1) / (NM - H);  // memory ops per MFMA
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          // the next stage's first fragments first (needed soonest), then the refill loads
-          const int op = i * PER + u;
-          if (op < NR) {
-            if (more) read_one(nbuf, 0, 0, op);
-          } else if (op < NR + NL) {
-            if (refill) issue_one(tl, tl.kb + kt + S, buf, op - NR);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      buf = nbuf;
-    }
-    }
+    };
+    if (tl.row_end - tl.row0 > wm0)
+      kloop(BoolC<true>{});
+    else
+      kloop(BoolC<false>{});
     __syncthreads();  // every wave is done with every buffer
 
     if (tl.slot >= 0) {
