@@ -387,13 +387,37 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   constexpr bool SPREAD = S >= 3;
   constexpr int PRO = SPREAD ? S - 1 : S;  // stages issued by an item's prologue
 
+  // With two stages, the next item's stage 0 is issued right after the K loop
+  // into buffer 0 while the epilogue stages its output through buffer 1 in two
+  // passes, then stage 1 follows. Every store of an epilogue is issued (range
+  // checks drop the ones outside C), so `pend`, the vector-memory operations
+  // issued after an item's stage 0, is known when the item starts.
+  constexpr bool EARLY = S == 2 && NW * EP_WAVE / 2 <= STAGE && TM % 2 == 0;
+  constexpr int PART_ST = TM * TN * 4;  // float32 partial-sum stores per wave
+  int pend = tl.kn > 1 ? NL : 0;
+  auto wait_pend = [&](int n) {
+    // at most `n` operations may remain in flight (vmcnt holds at most 63: waiting for
+    // fewer is only stricter)
+    if (n <= 0) wait_vmem<0>();
+    else if (n == NL) wait_vmem<(NL < 63 ? NL : 63)>();
+    else if (n == EP_ITERS) wait_vmem<(EP_ITERS < 63 ? EP_ITERS : 63)>();
+    else if (n == EP_ITERS + NL) wait_vmem<(EP_ITERS + NL < 63 ? EP_ITERS + NL : 63)>();
+    else if (n == PART_ST) wait_vmem<(PART_ST < 63 ? PART_ST : 63)>();
+    else if (n == PART_ST + NL) wait_vmem<(PART_ST + NL < 63 ? PART_ST + NL : 63)>();
+    else wait_vmem<0>();
+  };
+
   for (int item = 0; item < sk.n_items; ++item) {
     const int kn = tl.kn;
     // ---- wait for stage 0 of this item (and everything issued before it)
-    if (kn >= PRO)
-      wait_vmem<NL * (PRO - 1)>();
-    else
-      wait_vmem<0>();
+    if constexpr (EARLY) {
+      wait_pend(pend);
+    } else {
+      if (kn >= PRO)
+        wait_vmem<NL * (PRO - 1)>();
+      else
+        wait_vmem<0>();
+    }
     __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi)
@@ -532,6 +556,16 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
       kloop(BoolC<false>{});
     __syncthreads();  // every wave is done with every buffer
 
+    const bool has_next = item + 1 < sk.n_items;
+    Tile nx = tl;
+    if constexpr (EARLY) {
+      if (has_next) {
+        nx = make_item(item + 1);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) issue_one(nx, nx.kb, 0, i);
+      }
+    }
+
     if (tl.slot >= 0) {
       // ---- part of a split tile: float32 partial sums in the accumulator
       // layout (thread-major per MFMA register group, 16 bytes per lane)
@@ -548,62 +582,82 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
             *(f32x4*)(dst + ((int64_t)((mi * TN + ni) * 4 + gq) * (NW * kWave) + tid) * 4) = v;
           }
     } else {
-      // ---- epilogue through LDS: each wave stages its WTM x WTN piece as bf16 in
-      // its own region of the ring (row-major, 16-byte chunks XOR-swizzled by the
-      // row), then writes whole row segments to C with 16 bytes per lane.
-      lds_char* const ep = lds + wave * EP_WAVE;
+      // ---- epilogue through LDS: each wave stages its WTM x WTN piece as bf16
+      // in its own LDS region (row-major, 16-byte chunks XOR-swizzled by the
+      // row), then writes whole row segments to C with 16 bytes per lane. With
+      // EARLY the region lies in buffer 1 and the piece goes in two passes of
+      // WTM / 2 rows. Stores go through a buffer descriptor whose range ends at
+      // the group's last row; columns past N are sent out of range.
+      constexpr int PASSES = EARLY ? 2 : 1;
+      constexpr int PM = TM / PASSES;                        // MFMA row groups per pass
+      constexpr int P_ITERS = EP_ITERS / PASSES;             // 16-byte stores per lane per pass
+      lds_char* const ep = lds + (EARLY ? STAGE + wave * (EP_WAVE / 2) : wave * EP_WAVE);
+      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(C + tl.row0 * N), (short)0, (int)((tl.row_end - tl.row0) * N * 2), kBufferFlags);
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
+      for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
+        for (int m2 = 0; m2 < PM; ++m2)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            // lane holds row (lane & 31) of MFMA tile (mi, ni), columns 8 gq + 4 (lane >> 5) + 0..3
-            float v[4];
+          for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              v[qq] = acc[mi][ni][4 * gq + qq];
-              if (GELU) v[qq] = gelu_tanh(v[qq]);
+            for (int gq = 0; gq < 4; ++gq) {
+              const int mi = pass * PM + m2;
+              // lane holds row (lane & 31) of MFMA tile (mi, ni), columns 8 gq + 4 (lane >> 5) + 0..3
+              float v[4];
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                v[qq] = acc[mi][ni][4 * gq + qq];
+                if (GELU) v[qq] = gelu_tanh(v[qq]);
+              }
+              u32x2 o;
+              o[0] = pack_bf16x2(v[0], v[1]);
+              o[1] = pack_bf16x2(v[2], v[3]);
+              const int row = m2 * 32 + (lane & 31), ch = ni * 4 + gq;
+              *(__attribute__((address_space(3))) u32x2*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4) +
+                                                            (lane >> 5) * 8) = o;
+              __builtin_amdgcn_sched_barrier(0);  // bounds the live values of the GELU pass
             }
-            u32x2 o;
-            o[0] = pack_bf16x2(v[0], v[1]);
-            o[1] = pack_bf16x2(v[2], v[3]);
-            const int row = mi * 32 + (lane & 31), ch = ni * 4 + gq;
-            *(__attribute__((address_space(3))) u32x2*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4) +
-                                                          (lane >> 5) * 8) = o;
-            __builtin_amdgcn_sched_barrier(0);  // bounds the live values of the GELU pass
+        // LDS operations of one wave complete in order: no barrier between the
+        // wave's own writes and reads (nor before the next pass overwrites them)
+        constexpr int EP_G = P_ITERS < 4 ? P_ITERS : 4;  // reads in flight per group
+#pragma unroll
+        for (int it0 = 0; it0 < P_ITERS; it0 += EP_G) {
+          u32x4 v[EP_G];
+#pragma unroll
+          for (int u = 0; u < EP_G; ++u) {
+            const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
+            v[u] = *(__attribute__((address_space(3))) u32x4*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4));
           }
-      // LDS operations of one wave complete in order: no barrier between the
-      // wave's own writes and reads
-      constexpr int EP_G = EP_ITERS < 4 ? EP_ITERS : 4;  // reads in flight per group
 #pragma unroll
-      for (int it0 = 0; it0 < EP_ITERS; it0 += EP_G) {
-        u32x4 v[EP_G];
-#pragma unroll
-        for (int u = 0; u < EP_G; ++u) {
-          const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
-          v[u] = *(__attribute__((address_space(3))) u32x4*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4));
+          for (int u = 0; u < EP_G; ++u) {
+            const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
+            const int n = tl.n0 + wn0 + ch * 8;
+            const int off = n < N ? ((wm0 + pass * (WTM / PASSES) + row) * N + n) * 2 : 0x7FFFFFF0;
+            __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int u = 0; u < EP_G; ++u) {
-          const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
-          const int64_t grow = tl.row0 + wm0 + row;
-          const int n = tl.n0 + wn0 + ch * 8;
-          if (grow < tl.row_end && n < N) *(u32x4*)(C + grow * N + n) = v[u];
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- the next item's first stages (the ring is free once every wave has read its piece)
-    if (item + 1 < sk.n_items) {
+    if (has_next) {
       __syncthreads();
-      tl = make_item(item + 1);
+      if constexpr (EARLY) {
+        if (nx.kn > 1)
 #pragma unroll
-      for (int s2 = 0; s2 < PRO; ++s2)
-        if (s2 < tl.kn)
+          for (int i = 0; i < NL; ++i) issue_one(nx, nx.kb + 1, 1, i);
+        pend = (tl.slot >= 0 ? PART_ST : EP_ITERS) + (nx.kn > 1 ? NL : 0);
+        tl = nx;
+      } else {
+        tl = make_item(item + 1);
 #pragma unroll
-          for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);
+        for (int s2 = 0; s2 < PRO; ++s2)
+          if (s2 < tl.kn)
+#pragma unroll
+            for (int i = 0; i < NL; ++i) issue_one(tl, tl.kb + s2, s2, i);
+      }
     }
   }
 }
