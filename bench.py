@@ -27,15 +27,19 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def algorithmic_bytes(cfg):
-    """Bytes each phase must move at minimum (inputs read once, outputs written once)."""
+def algorithmic_bytes(cfg, gather):
+    """Bytes each phase must move at minimum (inputs read once, outputs written once).
+
+    With `gather` the permute phase only builds the index arrays and the FFN
+    phase reads the token rows from x itself (no permuted copy)."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k, de = cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert
     R = T * k
+    a_in = T * d * es if gather else R * d * es
     return {
         "route": T * d * es + d * E * es + R * 8,
-        "permute": R * 4 + T * d * es + R * 8 + R * d * es,
-        "ffn": R * d * es + 2 * E * d * de * es + 2 * R * de * es + R * d * es,
+        "permute": R * 4 + R * 8 + (0 if gather else T * d * es + R * d * es),
+        "ffn": a_in + 2 * E * d * de * es + 2 * R * de * es + R * d * es,
         "combine": R * d * es + R * 8 + T * d * es,
     }
 
@@ -158,6 +162,8 @@ def main():
     ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
     names = ["route", "permute", "ffn", "combine"]
+    # the stage calls moe_forward itself makes: bf16 folds the dispatch into the first GEMM
+    gather = cfg.dtype == "bf16" and cfg.T * cfg.d_model * 2 < 2 ** 31 - 1
 
     def stage_step(ev=None):
         if ev is not None:
@@ -165,11 +171,17 @@ def main():
         moe.moe_route(p, x, wr, b, None, bufs["idx"], bufs["gate"])
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_permute(p, bufs["idx"], x, bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"],
-                        bufs["x_perm"], ws_p)
+        if gather:
+            moe.moe_permute_index(p, bufs["idx"], bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"], ws_p)
+        else:
+            moe.moe_permute(p, bufs["idx"], x, bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"],
+                            bufs["x_perm"], ws_p)
         if ev is not None:
             ev[2].record(stream)
-        moe.moe_grouped_ffn(p, bufs["x_perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
+        if gather:
+            moe.moe_grouped_ffn_gather(p, x, bufs["perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
+        else:
+            moe.moe_grouped_ffn(p, bufs["x_perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
         if ev is not None:
             ev[3].record(stream)
         moe.moe_combine(p, bufs["y_perm"], bufs["inv"], bufs["gate"], bufs["y"])
@@ -202,14 +214,15 @@ def main():
     assert torch.equal(bufs["y"], layer.y), "stage path and moe_forward disagree"
 
     flops = cfg.ffn_flops()
-    bytes_ = algorithmic_bytes(cfg)
+    bytes_ = algorithmic_bytes(cfg, gather)
     t_ffn = phase_ms["ffn"] * 1e-3
     ffn_tflops = flops / t_ffn / 1e12
     if cfg.dtype == "bf16":
         roofline = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(cfg.name),
-                    "kernel": "grouped FFN phase: gemm_bf16_kernel x2 (GEMM1+GELU, GEMM2) + gemm_fixup_kernel x2"}
+                    "kernel": "grouped FFN phase: gemm_bf16_kernel x2 (GEMM1+GELU reading x through perm, GEMM2)"
+                              " + gemm_fixup_kernel x2"}
     else:
         gbs = bytes_["ffn"] / t_ffn / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",

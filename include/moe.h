@@ -119,6 +119,24 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const i
                              const void* W1, const void* W2, void* y_perm,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute without the row copy: counts, offsets, perm and inv as above,
+ * for callers that feed x itself to moe_grouped_ffn_gather.
+ *   ws at least moe_workspace_size(p, MOE_STAGE_PERMUTE) bytes */
+moe_status_t moe_permute_index(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* moe_grouped_ffn with the dispatch folded into the first GEMM: row r of the
+ * permuted input is read as x[perm[r]] (the same values moe_permute's x_perm
+ * holds), so no permuted copy of x is written or read; y_perm is the same,
+ * bit for bit, as moe_grouped_ffn gives on that x_perm.
+ *   x    [T, d_model], perm [T*k] int32 in [0, T) for rows in [0, offsets[E])
+ *   other arguments as for moe_grouped_ffn (same workspace size)
+ * MOE_ERR_UNSUPPORTED for float32 problems and when x spans 2 GiB or more. */
+moe_status_t moe_grouped_ffn_gather(const moe_problem_t* p, const void* x, const int32_t* perm,
+                                    const int32_t* offsets, const void* W1, const void* W2,
+                                    void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* Weighted combine (blog section 3 output formula; section 4, combine:
  * expert results return to their token):
  *   y[t] = sum over j < k of topk_gate[t, j] * y_perm[inv[t*k + j]]
@@ -129,7 +147,9 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32
                          const float* topk_gate, void* y, void* stream);
 
 /* The whole layer: route, permute, grouped FFN, combine on one stream, with
- * every intermediate in the workspace.
+ * every intermediate in the workspace. bf16 problems whose x spans less than
+ * 2 GiB take the moe_permute_index + moe_grouped_ffn_gather path (no x_perm
+ * copy); the result is the same either way.
  *   ws at least moe_workspace_size(p, MOE_STAGE_FORWARD) bytes */
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
                          const float* router_bias, const void* W1, const void* W2, void* y,

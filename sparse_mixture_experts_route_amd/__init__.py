@@ -20,7 +20,9 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_forward,
     moe_grouped_ffn,
+    moe_grouped_ffn_gather,
     moe_permute,
+    moe_permute_index,
     moe_route,
     moe_status_str,
     moe_workspace_size,

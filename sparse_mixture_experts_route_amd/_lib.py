@@ -41,6 +41,8 @@ def _load():
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp],
         "moe_permute": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_permute_index": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_grouped_ffn_gather": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [P, vp, vp, vp, vp, vp],
         "moe_forward": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
@@ -118,6 +120,18 @@ def moe_permute(p: Problem, topk_idx, x, counts, offsets, perm, inv, x_perm, ws,
 def moe_grouped_ffn(p: Problem, x_perm, offsets, W1, W2, y_perm, ws, stream=None):
     _check(_lib.moe_grouped_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(W2), _ptr(y_perm),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_permute_index(p: Problem, topk_idx, counts, offsets, perm, inv, ws, stream=None):
+    _check(_lib.moe_permute_index(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                                  _ptr(inv), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_permute_index")
+
+
+def moe_grouped_ffn_gather(p: Problem, x, perm, offsets, W1, W2, y_perm, ws, stream=None):
+    _check(_lib.moe_grouped_ffn_gather(ctypes.byref(p), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(W1), _ptr(W2),
+                                       _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_grouped_ffn_gather")
 
 
 def moe_combine(p: Problem, y_perm, inv, topk_gate, y, stream=None):

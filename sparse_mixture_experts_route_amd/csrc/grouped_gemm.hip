@@ -194,13 +194,17 @@ __device__ __forceinline__ SplitK split_k(int tiles, int nb, int j, int nk, int 
 
 // Block tile BM x BN over K steps of BK, a ring of S LDS stages, OCC blocks per
 // CU, WM x WN waves (each owns a (BM/WM) x (BN/WN) piece of the tile).
-template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU>
+// GATHER: row r of A is row perm[r] of a [a_rows, K] matrix (the first expert
+// GEMM reading the tokens straight from x, with no permuted copy).
+template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU, bool GATHER = false>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
                                                                       const int32_t* __restrict__ offsets,
                                                                       const bf16_bits* __restrict__ B,
                                                                       bf16_bits* __restrict__ C,
                                                                       float* __restrict__ partials, int64_t R, int K,
-                                                                      int N, int E, int n_tiles, int min_steps) {
+                                                                      int N, int E, int n_tiles, int min_steps,
+                                                                      const int32_t* __restrict__ perm,
+                                                                      int64_t a_rows) {
   constexpr int NW = WM * WN;                  // waves
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -275,6 +279,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     int64_t row0, row_end;
     i32x4 rsA, rsB;
     int kb, kn, slot;  // first K step, K steps, partial-sum slot (-1: the item completes the tile)
+    uint32_t ga[GATHER ? A_LD : 1];  // GATHER: per-lane byte offsets of the A loads in A
   };
   auto locate = [&](int t) {
     // expert e with tstart[e] <= t < tstart[e+1] (upper bound - 1)
@@ -293,7 +298,10 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     tl.n0 = n_tile * BN;
     // A: rows row0.. of the group; rows past the group's end fall outside the
     // descriptor's range and read as zero. B: the expert's [K, N] slab.
-    tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)((tl.row_end - tl.row0) * K * 2));
+    if constexpr (GATHER)
+      tl.rsA = buffer_rsrc(A, (uint32_t)(a_rows * K * 2));
+    else
+      tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)((tl.row_end - tl.row0) * K * 2));
     tl.rsB = buffer_rsrc(B + (int64_t)tl.e * K * N, (uint32_t)((int64_t)K * N * 2));
     tl.kb = 0;
     tl.kn = nk;
@@ -312,12 +320,32 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   };
   // per-lane byte offsets of the direct-to-LDS loads (A part does not depend on the tile)
   uint32_t a_off[A_LD];
+  int a_row[A_LD], a_c8[A_LD];  // row of the tile and first element of the lane's A piece
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int p = (wave * A_LD + i) * 64 + lane;  // LDS slot
     const int row = p / A_CH, c = (p % A_CH) ^ ((row / A_RPP) & (A_CH - 1));
     a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
+    a_row[i] = row;
+    a_c8[i] = c * 8;
   }
+  // GATHER: the token rows of a tile's A pieces (-1 past the group's end), and
+  // the byte offsets made from them; padding rows point past the range (read
+  // as zero, or as other rows of A: they are never stored)
+  auto load_perm = [&](const Tile& t_, int (&pv)[A_LD]) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int64_t r = t_.row0 + a_row[i];
+      pv[i] = r < t_.row_end ? perm[r] : -1;
+    }
+  };
+  auto set_ga = [&](Tile& t_, const int (&pv)[A_LD]) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i)
+        t_.ga[i] = pv[i] >= 0 ? (uint32_t)(((int64_t)pv[i] * K + a_c8[i]) * 2) : 0xFFFFFFF0u;
+    }
+  };
   uint32_t b_off0[B_LD];  // for n0 = 0
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   auto issue_one = [&](const Tile& tl, int kt, int buf, int i) {
     const uint32_t st = lds_base + buf * STAGE;
     if (i < A_LD)
-      buffer_load_lds16(tl.rsA, a_off[i], (uint32_t)kt * BK * 2, st + (wave * A_LD + i) * 1024);
+      buffer_load_lds16(tl.rsA, GATHER ? tl.ga[i] : a_off[i], (uint32_t)kt * BK * 2, st + (wave * A_LD + i) * 1024);
     else
       buffer_load_lds16(tl.rsB, b_off0[i - A_LD] + (uint32_t)tl.n0 * 2, (uint32_t)kt * BK * N * 2,
                         st + A_STAGE + (wave * B_LD + i - A_LD) * 1024);
@@ -372,6 +400,11 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   Tile tl;
   if (sk.n_items > 0) {
     tl = make_item(0);
+    if constexpr (GATHER) {
+      int pv[A_LD];
+      load_perm(tl, pv);
+      set_ga(tl, pv);
+    }
 #pragma unroll
     for (int s2 = 0; s2 < (S >= 3 ? S - 1 : S); ++s2)
       if (s2 < tl.kn)
@@ -426,6 +459,16 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
+    // GATHER: the next item's token rows are loaded now; their values are first
+    // used after this item's K loop, which ends with no load in flight
+    Tile nxt = tl;
+    int npv[A_LD];
+    if constexpr (GATHER) {
+      if (item + 1 < sk.n_items) {
+        nxt = make_item(item + 1);
+        load_perm(nxt, npv);
+      }
+    }
     // a wave whose whole slab of rows lies past the expert group's end (the
     // last, partly filled M tile of a group) skips its fragment reads and
     // MFMAs but still issues its share of the loads and joins the barriers;
@@ -560,7 +603,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     Tile nx = tl;
     if constexpr (EARLY) {
       if (has_next) {
-        nx = make_item(item + 1);
+        if constexpr (GATHER) {
+          nx = nxt;
+          set_ga(nx, npv);
+        } else {
+          nx = make_item(item + 1);
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) issue_one(nx, nx.kb, 0, i);
       }
@@ -651,7 +699,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
         pend = (tl.slot >= 0 ? PART_ST : EP_ITERS) + (nx.kn > 1 ? NL : 0);
         tl = nx;
       } else {
-        tl = make_item(item + 1);
+        if constexpr (GATHER) {
+          tl = nxt;
+          set_ga(tl, npv);
+        } else {
+          tl = make_item(item + 1);
+        }
 #pragma unroll
         for (int s2 = 0; s2 < PRO; ++s2)
           if (s2 < tl.kn)
@@ -875,7 +928,7 @@ constexpr int kFixupSub = 8;  // fixup blocks per split tile
 
 template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
-                       int K, int N, int E, bool gelu, hipStream_t s) {
+                       int K, int N, int E, bool gelu, const int32_t* perm, int64_t a_rows, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
   const int64_t tiles_ub = tiles_upper_bound(R, N, E, BM, BN);
   if (tiles_ub > INT32_MAX || K % BK != 0) return hipErrorInvalidValue;
@@ -889,17 +942,24 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   // split leftover tiles number at most nb / 3 per XCD, and none when K is short (split_leftover)
   const unsigned fix_grid = nk >= min_steps ? (unsigned)(8 * (nb / 3) * kFixupSub) : 0u;
   constexpr int NT = WM * WN * 64;
-  if (gelu) {
+  if (gelu && perm) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true, true>), dim3((unsigned)grid), dim3(NT), 0,
+                       s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
+                       n_tiles, min_steps, perm, a_rows);
+    if (fix_grid)
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+  } else if (gelu) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps);
+                       n_tiles, min_steps, nullptr, R);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps);
+                       n_tiles, min_steps, nullptr, R);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
@@ -957,7 +1017,10 @@ size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
 }
 
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s) {
+                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
+                               const int32_t* perm, int64_t a_rows) {
+  if (perm && (dtype != MOE_DTYPE_BF16 || !gelu || a_rows * K * 2 >= (int64_t)INT32_MAX))
+    return hipErrorInvalidValue;  // row gathering: first bf16 GEMM, A addressable with 31-bit offsets
   if (dtype == MOE_DTYPE_F32) {
     const int n_tiles = (int)ceil_div(N, F_BN);
     const int64_t m_tiles = (R + (int64_t)E * (F_BM - 1)) / F_BM;
@@ -973,19 +1036,19 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
   }
   switch (pick_tile(R, K, N, E)) {
     case 0:
-      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 1:
-      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 2:
-      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 3:
-      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 4:
-      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 5:
-      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     default:
-      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, s);
+      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
   }
 }
 

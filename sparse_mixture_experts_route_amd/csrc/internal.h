@@ -29,8 +29,11 @@ hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* i
 // C[r] = act(A[r] B[e]) for rows r of every expert group e (offsets[E+1]).
 // A [R, K], B [E, K, N], C [R, N]; act = GELU_tanh or identity. `partials` is
 // workspace of grouped_gemm_partials_bytes() for split tiles (bf16 path).
+// With `perm` (bf16, gelu only) row r of A is row perm[r] of A [a_rows, K];
+// returns hipErrorInvalidValue when a_rows * K * 2 does not fit in 31 bits.
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s);
+                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
+                               const int32_t* perm = nullptr, int64_t a_rows = 0);
 
 // Host-only bound of the partial-sum workspace one launch_grouped_gemm call may use.
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);

@@ -115,6 +115,12 @@ inline char* align_ws(void* ws) { return (char*)(((uintptr_t)ws + kAlign - 1) / 
 
 inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The first GEMM reads x rows through perm with 32-bit byte offsets into x
+// (bf16 path only).
+inline bool gather_supported(const moe_problem_t& p) {
+  return p.dtype == MOE_DTYPE_BF16 && p.T * (int64_t)p.d_model * 2 < (int64_t)INT32_MAX;
+}
+
 }  // namespace
 
 MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes) {
@@ -156,6 +162,44 @@ MOE_API moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx
   hipError_t e = moe::launch_permute_index(*p, topk_idx, counts, offsets, perm, inv, w.blockcounts, w.blockbase, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_gather(*p, x, inv, x_perm, s));
+}
+
+MOE_API moe_status_t moe_permute_index(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) || !aligned16(inv) ||
+      !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_PERMUTE)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const PermuteWs w = carve_permute(c, *p);
+  return hip_status(moe::launch_permute_index(*p, topk_idx, counts, offsets, perm, inv, w.blockcounts,
+                                              w.blockbase, (hipStream_t)stream));
+}
+
+MOE_API moe_status_t moe_grouped_ffn_gather(const moe_problem_t* p, const void* x, const int32_t* perm,
+                                            const int32_t* offsets, const void* W1, const void* W2, void* y_perm,
+                                            void* ws, size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !perm || !offsets || !W1 || !W2 || !y_perm || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(perm) || !aligned16(offsets) || !aligned16(W1) || !aligned16(W2) ||
+      !aligned16(y_perm) || !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!gather_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_GROUPED_FFN)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const FfnWs fw = carve_ffn(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = p->T * p->k;
+  hipError_t e = moe::launch_grouped_gemm(p->dtype, x, offsets, W1, fw.h, fw.partials, R, p->d_model,
+                                          p->d_expert, p->E, true, s, perm, p->T);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, R, p->d_expert,
+                                             p->d_model, p->E, false, s));
 }
 
 MOE_API moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
@@ -206,10 +250,17 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
   hipError_t e = moe::launch_route(*p, x, w_router, router_bias, nullptr, w.idx, w.gate, s);
   if (e == hipSuccess)
     e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts, w.pw.blockbase, s);
-  if (e == hipSuccess) e = moe::launch_gather(*p, x, w.inv, w.x_perm, s);
-  if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model,
-                                 p->d_expert, p->E, true, s);
+  if (gather_supported(*p)) {
+    // dispatch folded into the first GEMM: its A rows are read as x[perm[r]]
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model, p->d_expert,
+                                   p->E, true, s, w.perm, p->T);
+  } else {
+    if (e == hipSuccess) e = moe::launch_gather(*p, x, w.inv, w.x_perm, s);
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model,
+                                   p->d_expert, p->E, true, s);
+  }
   if (e == hipSuccess)
     e = moe::launch_grouped_gemm(p->dtype, w.fw.h, w.offsets, W2, w.y_perm, w.fw.partials, R, p->d_expert,
                                  p->d_model, p->E, false, s);

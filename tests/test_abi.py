@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-        "moe_forward", "moe_status_str"])
+        "moe_workspace_size", "moe_route", "moe_permute", "moe_permute_index", "moe_grouped_ffn",
+        "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_status_str"])
 
 
 def test_library_exports_every_declared_symbol(libmoe_path):
@@ -124,3 +124,21 @@ def test_binding_refuses_host_tensors(moe):
     x = torch.zeros(64, 128)
     with pytest.raises(ValueError):
         moe.moe_route(p, x, x, None, None, x, x)
+
+
+def test_permute_index_and_ffn_gather_reject_before_launch(moe, lib):
+    p = P(moe)
+    s = ctypes.c_void_p(0)
+    need_p = moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE)
+    need_f = moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN)
+    assert lib.moe_permute_index(ctypes.byref(p), None, A, A, A, A, A2, need_p, s) == INVALID
+    assert lib.moe_permute_index(ctypes.byref(p), A, A, A, MIS, A, A2, need_p, s) == INVALID
+    assert lib.moe_permute_index(ctypes.byref(p), A, A, A, A, A, A2, need_p - 1, s) == WS_SMALL
+    assert lib.moe_grouped_ffn_gather(ctypes.byref(p), A, None, A, A, A, A, A2, need_f, s) == INVALID
+    assert lib.moe_grouped_ffn_gather(ctypes.byref(p), A, A, A, A, MIS, A, A2, need_f, s) == INVALID
+    assert lib.moe_grouped_ffn_gather(ctypes.byref(p), A, A, A, A, A, A, A2, need_f - 1, s) == WS_SMALL
+    # float32 problems, and x of 2 GiB or more, are outside the gathering path
+    f32 = P(moe, dtype=0)
+    assert lib.moe_grouped_ffn_gather(ctypes.byref(f32), A, A, A, A, A, A, A2, 1 << 40, s) == UNSUPPORTED
+    big = P(moe, T=1 << 20, d=1024, k=1)
+    assert lib.moe_grouped_ffn_gather(ctypes.byref(big), A, A, A, A, A, A, A2, 1 << 40, s) == UNSUPPORTED

@@ -113,3 +113,43 @@ def test_rows_past_offsets_end_untouched(moe):
     assert torch.isnan(y[420:].float()).all()
     ref = oracle_ffn("bf16", x_perm[:420], off, W1, W2)
     assert rel_err(f64(y[:420]), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("tile,split0", [("auto", False), ("256x256w8", True), ("128x128", False),
+                                         ("256x128", True), ("256x256w8k32", False)])
+def test_gather_path_matches_permuted_copy(moe, tile, split0):
+    """moe_permute_index + moe_grouped_ffn_gather (the first GEMM reads x[perm[r]])
+    give the same index arrays and the same y_perm, bit for bit, as moe_permute
+    + moe_grouped_ffn on the copied x_perm."""
+    from harness import make_inputs, scaled_config
+    cfg = scaled_config("skewed", T=1500, d_model=256, E=16, k=4, d_expert=320)
+    announce(f"ffn gather {tile} split0={split0}")
+    inp = make_inputs(cfg, seed=3, device="cuda")
+    layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, inp["x"].dtype)
+    p = layer.problem
+    env = {"MOE_GEMM_MAX_BLOCKS": "24"}
+    if tile != "auto":
+        env["MOE_GEMM_TILE"] = tile
+    if split0:
+        env["MOE_GEMM_SPLIT_MIN_STEPS"] = "0"
+    os.environ.update(env)
+    try:
+        st = layer.stages(inp["x"], inp["w_router"], inp["W1"], inp["W2"], inp["router_bias"])
+        R = cfg.T * cfg.k
+        dev = "cuda"
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+        perm = torch.empty(R, dtype=torch.int32, device=dev)
+        inv = torch.empty(R, dtype=torch.int32, device=dev)
+        ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
+        y_perm = torch.full((R, cfg.d_model), float("nan"), dtype=inp["x"].dtype, device=dev)
+        moe.moe_permute_index(p, st["idx"], counts, offsets, perm, inv, ws_p)
+        moe.moe_grouped_ffn_gather(p, inp["x"], perm, offsets, inp["W1"], inp["W2"], y_perm, ws_f)
+        torch.cuda.synchronize()
+    finally:
+        for key in env:
+            del os.environ[key]
+    for name, t in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
+        assert torch.equal(t, st[name]), name
+    assert torch.equal(y_perm, st["y_perm"])
