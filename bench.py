@@ -161,6 +161,7 @@ def main():
     bufs = layer.stages(x, wr, W1, W2, b, logits=False)  # allocates the stage outputs once
     ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
     names = ["route", "permute", "ffn", "combine"]
     # the stage calls moe_forward itself makes: bf16 folds the dispatch into the first GEMM
     gather = cfg.dtype == "bf16" and cfg.T * cfg.d_model * 2 < 2 ** 31 - 1
@@ -168,7 +169,7 @@ def main():
     def stage_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_route(p, x, wr, b, None, bufs["idx"], bufs["gate"])
+        moe.moe_route_ws(p, x, wr, b, None, bufs["idx"], bufs["gate"], ws_r)
         if ev is not None:
             ev[1].record(stream)
         if gather:

@@ -60,7 +60,8 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 typedef enum {
   MOE_STAGE_PERMUTE = 0,
   MOE_STAGE_GROUPED_FFN = 1,
-  MOE_STAGE_FORWARD = 2
+  MOE_STAGE_FORWARD = 2,
+  MOE_STAGE_ROUTE = 3
 } moe_stage_t;
 
 typedef struct {
@@ -73,7 +74,7 @@ typedef struct {
 } moe_problem_t;
 
 /* Workspace bytes that `stage` needs for problem `p` (host only, no HIP call).
- * moe_route and moe_combine need none. */
+ * moe_route and moe_combine need none; moe_route_ws takes MOE_STAGE_ROUTE. */
 moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes);
 
 /* Router Linear + Softmax + top-k (blog section 3, structure: the gating
@@ -87,6 +88,20 @@ moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* b
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
                        const float* router_bias, float* logits, int32_t* topk_idx,
                        float* topk_gate, void* stream);
+
+/* moe_route with a workspace (same arguments and results). When the tokens
+ * alone give too few blocks to fill the GPU (small T: decode-sized batches,
+ * where the MOSAIC summary's performance model, method item 2, singles out
+ * dispatch latency), the bf16 contraction is split over d_model: blocks write
+ * float32 partial logits to ws and a second launch adds them in a fixed order
+ * (deterministic), adds the bias and selects. The selection then sees logits
+ * summed in another order than moe_route's, so near-ties may resolve
+ * differently between the two.
+ *   ws at least moe_workspace_size(p, MOE_STAGE_ROUTE) bytes (may be 1 byte
+ *   when no split is used; ws must still be non-NULL and 16-byte aligned) */
+moe_status_t moe_route_ws(const moe_problem_t* p, const void* x, const void* w_router,
+                          const float* router_bias, float* logits, int32_t* topk_idx,
+                          float* topk_gate, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch as a local permutation (blog section 4, dispatch: each token is
  * sent to the expert it chose). Rows are grouped by expert; inside a group

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_STAGE_FORWARD,
     MOE_STAGE_GROUPED_FFN,
     MOE_STAGE_PERMUTE,
+    MOE_STAGE_ROUTE,
     MoEError,
     Problem,
     lib_path,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     moe_permute,
     moe_permute_index,
     moe_route,
+    moe_route_ws,
     moe_status_str,
     moe_workspace_size,
 )

@@ -17,6 +17,7 @@ MOE_DTYPE_BF16 = 1
 MOE_STAGE_PERMUTE = 0
 MOE_STAGE_GROUPED_FFN = 1
 MOE_STAGE_FORWARD = 2
+MOE_STAGE_ROUTE = 3
 
 
 class MoEError(RuntimeError):
@@ -39,6 +40,7 @@ def _load():
     sigs = {
         "moe_workspace_size": [P, i32, ctypes.POINTER(sz)],
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp],
+        "moe_route_ws": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute_index": [P, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -109,6 +111,12 @@ def moe_workspace_size(p: Problem, stage: int) -> int:
 def moe_route(p: Problem, x, w_router, router_bias, logits, topk_idx, topk_gate, stream=None):
     _check(_lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(logits),
                           _ptr(topk_idx), _ptr(topk_gate), _stream(stream)), "moe_route")
+
+
+def moe_route_ws(p: Problem, x, w_router, router_bias, logits, topk_idx, topk_gate, ws, stream=None):
+    _check(_lib.moe_route_ws(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(logits),
+                             _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "moe_route_ws")
 
 
 def moe_permute(p: Problem, topk_idx, x, counts, offsets, perm, inv, x_perm, ws, stream=None):

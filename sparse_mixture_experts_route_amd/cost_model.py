@@ -262,6 +262,7 @@ def measure(T: int, d_model: int, E: int, k: int, d_expert: int, steps: int = 10
     perm, inv = torch.empty(R, **i32), torch.empty(R, **i32)
     y_perm = torch.empty((R, d_model), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, d_model), dtype=torch.bfloat16, device=dev)
+    ws_r = torch.empty(lib.moe_workspace_size(p, lib.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
     ws_p = torch.empty(lib.moe_workspace_size(p, lib.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(lib.moe_workspace_size(p, lib.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -269,7 +270,7 @@ def measure(T: int, d_model: int, E: int, k: int, d_expert: int, steps: int = 10
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        lib.moe_route(p, x, wr, None, None, idx, gate)
+        lib.moe_route_ws(p, x, wr, None, None, idx, gate, ws_r)
         if ev:
             ev[1].record(stream)
         lib.moe_permute_index(p, idx, counts, offsets, perm, inv, ws_p)

@@ -167,15 +167,19 @@ struct SplitK {
 
 constexpr int kSplitMinSteps = 24;
 
-__host__ __device__ __forceinline__ bool split_leftover(int rem, int nb, int nk, int min_steps) {
-  return rem > 0 && rem * 3 <= nb && (int64_t)nk * (nb - rem) >= (int64_t)min_steps * nb;
+// `max_rem` caps the leftover tiles that may be split: nb / 3 for the tiles
+// that fill the matrix cores, nb - 1 for the small-M tile of decode-sized
+// batches, whose one partly filled round would otherwise leave most blocks
+// idle while a few stream whole weight slabs.
+__host__ __device__ __forceinline__ bool split_leftover(int rem, int nb, int nk, int min_steps, int max_rem) {
+  return rem > 0 && rem <= max_rem && (int64_t)nk * (nb - rem) >= (int64_t)min_steps * nb;
 }
 
-__device__ __forceinline__ SplitK split_k(int tiles, int nb, int j, int nk, int min_steps) {
+__device__ __forceinline__ SplitK split_k(int tiles, int nb, int j, int nk, int min_steps, int max_rem) {
   SplitK r;
   r.full = tiles / nb;
   r.rem = tiles - r.full * nb;
-  if (!split_leftover(r.rem, nb, nk, min_steps)) {
+  if (!split_leftover(r.rem, nb, nk, min_steps, max_rem)) {
     r.full += j < r.rem ? 1 : 0;  // one more round of whole tiles for the first rem blocks
     r.rem = 0;
     r.s0 = r.s1 = 0;
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
                                                                       bf16_bits* __restrict__ C,
                                                                       float* __restrict__ partials, int64_t R, int K,
                                                                       int N, int E, int n_tiles, int min_steps,
+                                                                      int max_rem,
                                                                       const int32_t* __restrict__ perm,
                                                                       int64_t a_rows) {
   constexpr int NW = WM * WN;                  // waves
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   const int nk = K / BK;
   // whole tiles for `full` rounds, then the K steps of the `rem` leftover tiles
   // split evenly over the XCD's blocks (stream-K)
-  const SplitK sk = split_k(hi - lo, nb, j, nk, min_steps);
+  const SplitK sk = split_k(hi - lo, nb, j, nk, min_steps, max_rem);
 
   lds_char* const lds = (lds_char*)smem;
   const uint32_t lds_base = lds_addr(smem);
@@ -724,94 +729,105 @@ template <int BM, int BN, int WM, int WN, int SUB, bool GELU>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restrict__ offsets,
                                                          const float* __restrict__ partials,
                                                          bf16_bits* __restrict__ C, int64_t R, int nk, int N,
-                                                         int E, int n_tiles, int nb, int min_steps) {
+                                                         int E, int n_tiles, int nb, int min_steps,
+                                                         int max_rem) {
   constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
   constexpr int ENT = BM * BN / 4;           // float32x4 entries per slot
   constexpr int PER = ENT / SUB / 256;       // entries per thread
   static_assert(PER * SUB * 256 == ENT, "fixup split");
-  constexpr int kMaxSlots = 64;  // >= blocks per XCD of any launch (kMaxCUs / 8 * 2)
+  constexpr int kMaxSlots = 64;  // >= blocks per XCD of any launch (kMaxCUs / 8 * 2), one lane each
   __shared__ int s_tstart[257];
   __shared__ int s_mtiles[256];
   __shared__ int s_slots[kMaxSlots];
   __shared__ int s_nslots;
 
-  const int b = blockIdx.x % SUB, x = (blockIdx.x / SUB) % 8, r = blockIdx.x / SUB / 8;
+  // block (b, x, r0) takes part b of leftover tiles r0, r0 + rstep, ... of XCD x
+  const int b = blockIdx.x % SUB, x = (blockIdx.x / SUB) % 8, r0 = blockIdx.x / SUB / 8;
+  const int rstep = gridDim.x / (SUB * 8);
   build_tile_list<BM>(offsets, E, R, n_tiles, s_tstart, s_mtiles);
   const int total = s_tstart[E];
   const int lo = (int)((int64_t)total * x / 8), hi = (int)((int64_t)total * (x + 1) / 8);
   const int full = (hi - lo) / nb, rem = (hi - lo) - full * nb;
-  if (r >= rem || !split_leftover(rem, nb, nk, min_steps)) return;
-  const int64_t W = (int64_t)rem * nk, u0 = (int64_t)r * nk, u1 = u0 + nk;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int jj = 0; jj < nb; ++jj) {
-      const int64_t s0 = W * jj / nb, s1 = W * (jj + 1) / nb;
-      if (s0 >= u1) break;
-      if (s1 <= u0 || s1 <= s0) continue;
-      if (s0 <= u0 && s1 >= u1) {  // one block ran the whole tile and stored it
-        n = -1;
-        break;
+  if (!split_leftover(rem, nb, nk, min_steps, max_rem)) return;
+  for (int r = r0; r < rem; r += rstep) {
+    const int64_t W = (int64_t)rem * nk, u0 = (int64_t)r * nk, u1 = u0 + nk;
+    // lane jj of wave 0 checks block jj's share [s0, s1) of the units (nb <= kMaxSlots = 64 lanes);
+    // the slots of the blocks that touch tile r, in block (= K) order
+    if (threadIdx.x < kWave) {
+      const int jj = threadIdx.x;
+      bool touch = false, whole = false;
+      int slot = 0;
+      if (jj < nb) {
+        const int64_t s0 = W * jj / nb, s1 = W * (jj + 1) / nb;
+        touch = s1 > s0 && s0 < u1 && s1 > u0;
+        whole = touch && s0 <= u0 && s1 >= u1;  // one block ran the whole tile and stored it
+        slot = (jj * 8 + x) * 2 + (r - (int)(s0 / nk));
       }
-      if (n < kMaxSlots) s_slots[n] = (jj * 8 + x) * 2 + (r - (int)(s0 / nk));
-      ++n;
+      const uint64_t tm = __ballot(touch), wm = __ballot(whole);  // every lane of wave 0 votes
+      const int pos = __popcll(tm & ((1ull << jj) - 1ull));
+      if (touch) s_slots[pos] = slot;
+      if (jj == 0) s_nslots = wm ? -1 : __popcll(tm);
     }
-    s_nslots = n;
-  }
-  __syncthreads();
-  const int ns = s_nslots;
-  if (ns <= 0) return;
+    __syncthreads();
+    const int ns = s_nslots;
+    if (ns <= 0) {
+      __syncthreads();  // s_slots is rewritten for the next tile
+      continue;
+    }
 
-  // the tile: same enumeration as the GEMM kernel
-  const int t = lo + full * nb + r;
-  int a0 = 0, a1 = E;
-  while (a1 - a0 > 1) {
-    const int mid = (a0 + a1) >> 1;
-    if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
-  }
-  const int e = a0, local = t - s_tstart[e], mt = s_mtiles[e];
-  const int n_tile = local / mt, m_idx = local - n_tile * mt;
-  const int64_t row0 = (int64_t)offsets[e] + (int64_t)m_idx * BM;
-  const int64_t row_end = min((int64_t)offsets[e + 1], R);
-  const int n0 = n_tile * BN;
+    // the tile: same enumeration as the GEMM kernel
+    const int t = lo + full * nb + r;
+    int a0 = 0, a1 = E;
+    while (a1 - a0 > 1) {
+      const int mid = (a0 + a1) >> 1;
+      if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
+    }
+    const int e = a0, local = t - s_tstart[e], mt = s_mtiles[e];
+    const int n_tile = local / mt, m_idx = local - n_tile * mt;
+    const int64_t row0 = (int64_t)offsets[e] + (int64_t)m_idx * BM;
+    const int64_t row_end = min((int64_t)offsets[e + 1], R);
+    const int n0 = n_tile * BN;
 
-  f32x4 acc[PER];
+    f32x4 acc[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ebase = b * (ENT / SUB) + threadIdx.x;
-  // slots in K order, four at a time so that their loads are in flight together
-  for (int si = 0; si < ns; si += 4) {
-    f32x4 v[4][PER];
+    for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ebase = b * (ENT / SUB) + threadIdx.x;
+    // slots in K order, four at a time so that their loads are in flight together
+    for (int si = 0; si < ns; si += 4) {
+      f32x4 v[4][PER];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int sl = si + q4 < ns ? s_slots[si + q4] : -1;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int sl = si + q4 < ns ? s_slots[si + q4] : -1;
 #pragma unroll
-      for (int u = 0; u < PER; ++u)
-        v[q4][u] = sl >= 0 ? ((const f32x4*)(partials + (int64_t)sl * (BM * BN)))[ebase + u * 256]
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < PER; ++u)
+          v[q4][u] = sl >= 0 ? ((const f32x4*)(partials + (int64_t)sl * (BM * BN)))[ebase + u * 256]
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
     }
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
+    for (int u = 0; u < PER; ++u) {
+      // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
+      const int en = ebase + u * 256, grp = en / (NW * kWave), tt = en % (NW * kWave);
+      const int mi = grp / (TN * 4), ni = (grp / 4) % TN, gq = grp % 4;
+      const int wave = tt / kWave, lane = tt % kWave;
+      const int row = (wave / WN) * WTM + mi * 32 + (lane & 31);
+      const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
+      const int64_t grow = row0 + row;
+      const int n = n0 + col;
+      if (grow >= row_end || n >= N) continue;
+      float v[4];
 #pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
-    const int en = ebase + u * 256, grp = en / (NW * kWave), tt = en % (NW * kWave);
-    const int mi = grp / (TN * 4), ni = (grp / 4) % TN, gq = grp % 4;
-    const int wave = tt / kWave, lane = tt % kWave;
-    const int row = (wave / WN) * WTM + mi * 32 + (lane & 31);
-    const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
-    const int64_t grow = row0 + row;
-    const int n = n0 + col;
-    if (grow >= row_end || n >= N) continue;
-    float v[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];
-    u32x2 o;
-    o[0] = pack_bf16x2(v[0], v[1]);
-    o[1] = pack_bf16x2(v[2], v[3]);
-    *(u32x2*)(C + grow * N + n) = o;
+      for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];
+      u32x2 o;
+      o[0] = pack_bf16x2(v[0], v[1]);
+      o[1] = pack_bf16x2(v[2], v[3]);
+      *(u32x2*)(C + grow * N + n) = o;
+    }
+    __syncthreads();  // s_slots is rewritten for the next tile
   }
 }
 
@@ -880,6 +896,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // can share one split tile (gemm_fixup_kernel's slot list)
 constexpr int kMaxCUs = 256;
 
+}  // namespace
+
 int device_cus() {
   static int cus = 0;
   if (!cus) {
@@ -892,11 +910,14 @@ int device_cus() {
   return cus;
 }
 
+namespace {
+
 // Tile configurations of the bf16 path: block tile, K step, LDS ring stages,
 // blocks per CU. LDS per block = stages * (BM + BN) * BK * 2 bytes.
 struct TileShape {
   const char* name;
   int bm, bn, bk, stages, occ;
+  bool fill;  // decode-sized batches: a block per CU slot, any partial round split
 };
 constexpr TileShape kShapes[] = {
     {"256x256", 256, 256, 64, 2, 1},     // 128 KB
@@ -906,17 +927,20 @@ constexpr TileShape kShapes[] = {
     {"128x128k32", 128, 128, 32, 4, 2},  // 64 KB
     {"256x256w8", 256, 256, 64, 2, 1},   // 128 KB, 8 waves
     {"256x256w8k32", 256, 256, 32, 4, 1},  // 128 KB, 8 waves
+    {"32x256", 32, 256, 64, 4, 1, true},  // 144 KB, 4 waves of 32 x 64: weight streaming
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
+constexpr int kDecodeTile = 7;
 
 // persistent grid: OCC blocks per CU, a multiple of 8 so every XCD holds the
-// same number of blocks. MOE_GEMM_MAX_BLOCKS=<n> lowers the cap (several
-// rounds of tiles on small problems: exercises the leftover-tile split).
-int64_t persistent_grid(int64_t tiles_ub, int occ) {
+// same number of blocks; with `fill` every slot, so that split tiles spread
+// over the whole GPU. MOE_GEMM_MAX_BLOCKS=<n> lowers the cap (several rounds
+// of tiles on small problems: exercises the leftover-tile split).
+int64_t persistent_grid(int64_t tiles_ub, int occ, bool fill = false) {
   int64_t slots = (int64_t)device_cus() / 8 * 8 * occ;
   const char* cap = getenv("MOE_GEMM_MAX_BLOCKS");
   if (cap && cap[0]) slots = min(slots, max((int64_t)8, (int64_t)atoi(cap) / 8 * 8));
-  return max((int64_t)8, min(ceil_div(tiles_ub, 8) * 8, slots));
+  return max((int64_t)8, fill ? slots : min(ceil_div(tiles_ub, 8) * 8, slots));
 }
 
 int64_t tiles_upper_bound(int64_t R, int N, int E, int bm, int bn) {
@@ -924,45 +948,49 @@ int64_t tiles_upper_bound(int64_t R, int N, int E, int bm, int bn) {
   return m_tiles * ceil_div(N, bn);
 }
 
-constexpr int kFixupSub = 8;  // fixup blocks per split tile
+constexpr int kFixupSub = 8;     // fixup blocks per split tile
+constexpr int kFixupRounds = 4;  // split tiles one fixup block may take in turn
 
-template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2>
+template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2, bool FILL = false>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
                        int K, int N, int E, bool gelu, const int32_t* perm, int64_t a_rows, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
   const int64_t tiles_ub = tiles_upper_bound(R, N, E, BM, BN);
   if (tiles_ub > INT32_MAX || K % BK != 0) return hipErrorInvalidValue;
-  const int64_t grid = persistent_grid(tiles_ub, OCC);
+  const int64_t grid = persistent_grid(tiles_ub, OCC, FILL);
   const int nb = (int)(grid / 8);
   const int nk = K / BK;
   // MOE_GEMM_SPLIT_MIN_STEPS=<n> overrides the split threshold (0: split every small leftover)
   int min_steps = kSplitMinSteps;
   const char* ms = getenv("MOE_GEMM_SPLIT_MIN_STEPS");
   if (ms && ms[0]) min_steps = max(0, atoi(ms));
-  // split leftover tiles number at most nb / 3 per XCD, and none when K is short (split_leftover)
-  const unsigned fix_grid = nk >= min_steps ? (unsigned)(8 * (nb / 3) * kFixupSub) : 0u;
+  // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
+  const int max_rem = FILL ? nb - 1 : nb / 3;
+  // fixup blocks: kFixupSub per split tile, each looping over up to kFixupRounds tiles
+  const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
+  const unsigned fix_grid = nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * kFixupSub) : 0u;
   constexpr int NT = WM * WN * 64;
   if (gelu && perm) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true, true>), dim3((unsigned)grid), dim3(NT), 0,
                        s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, perm, a_rows);
+                       n_tiles, min_steps, max_rem, perm, a_rows);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else if (gelu) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, nullptr, R);
+                       n_tiles, min_steps, max_rem, nullptr, R);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, nullptr, R);
+                       n_tiles, min_steps, max_rem, nullptr, R);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   }
   return hipGetLastError();
 }
@@ -978,7 +1006,10 @@ int pick_tile(int64_t R, int K, int N, int E) {
   if (force && force[0])
     for (int c = 0; c < kNumShapes; ++c)
       if (!strcmp(force, kShapes[c].name)) return c;
-  const double tile_eff[kNumShapes] = {0.0, 0.0, 0.8, 0.75, 0.0, 1.0, 0.0};
+  // decode-sized batches (at most ~40 rows per expert on average): the weight
+  // slabs dominate; 32-row tiles stream them from every CU
+  if (R <= 40 * (int64_t)E && K % 64 == 0) return kDecodeTile;
+  const double tile_eff[kNumShapes] = {0.0, 0.0, 0.8, 0.75, 0.0, 1.0, 0.0, 0.0};
   const double cus = device_cus();
   int best = 5;
   double best_score = -1.0;
@@ -1012,7 +1043,7 @@ int pick_tile(int64_t R, int K, int N, int E) {
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
   if (dtype != MOE_DTYPE_BF16) return 0;
   const TileShape& ts = kShapes[pick_tile(R, K, N, E)];
-  const int64_t grid = persistent_grid(tiles_upper_bound(R, N, E, ts.bm, ts.bn), ts.occ);
+  const int64_t grid = persistent_grid(tiles_upper_bound(R, N, E, ts.bm, ts.bn), ts.occ, ts.fill);
   return (size_t)grid * 2 * ts.bm * ts.bn * sizeof(float);  // two split segments per block at most
 }
 
@@ -1047,6 +1078,9 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
       return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
     case 5:
       return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+    case kDecodeTile:
+      return launch_bf16<32, 256, 64, 4, 1, 1, 4, true>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows,
+                                                        s);
     default:
       return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
   }

@@ -10,11 +10,34 @@
 namespace moe {
 
 constexpr int kPermuteTokensPerBlock = 256;
+// batches of at most this many tokens (and k <= 8) are permuted by one workgroup
+constexpr int kSmallPermuteT = 1024;
+// ... and with at most this many, that workgroup also completes a split router
+constexpr int kFusedRouteT = 16;
 
 inline int64_t permute_blocks(int64_t T) { return (T + kPermuteTokensPerBlock - 1) / kPermuteTokensPerBlock; }
 
+// Multiprocessor count of the current device (at most 256; 256 when unknown).
+int device_cus();
+
+// Router. With `part` (route_partials_bytes(p) bytes, float32) the bf16 path
+// splits the contraction over d_model when the token blocks alone do not fill
+// the GPU (route_splits(p) > 1) and finishes with a second launch.
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* w_router, const float* bias,
-                        float* logits, int32_t* idx, float* gate, hipStream_t s);
+                        float* logits, int32_t* idx, float* gate, float* part, hipStream_t s);
+int route_splits(const moe_problem_t& p);
+size_t route_partials_bytes(const moe_problem_t& p);
+// The first launch of a split router alone (route_splits(p) > 1 required):
+// float32 partial logits to part.
+hipError_t launch_route_partials(const moe_problem_t& p, const void* x, const void* w_router, float* part,
+                                 hipStream_t s);
+// Decode-sized batches (route_permute_fused(p)): one workgroup completes a
+// split router from its partial logits (idx, gate as launch_route would give
+// them) and permutes (counts, offsets, perm, inv as launch_permute_index).
+bool route_permute_fused(const moe_problem_t& p);
+hipError_t launch_finalize_permute_small(const moe_problem_t& p, const float* part, int nsplit, const float* bias,
+                                        int32_t* idx, float* gate, int32_t* counts, int32_t* offsets,
+                                        int32_t* perm, int32_t* inv, hipStream_t s);
 
 // counts/offsets/perm/inv from the routing table; blockcounts/blockbase are
 // workspace arrays of permute_blocks(T) * E int32 each.

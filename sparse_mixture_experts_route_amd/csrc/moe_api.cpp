@@ -70,9 +70,15 @@ FfnWs carve_ffn(Carver& c, const moe_problem_t& p) {
   return w;
 }
 
+// float32 partial logits of a router split over d_model (none when unsplit)
+float* carve_route(Carver& c, const moe_problem_t& p) {
+  const size_t n = moe::route_partials_bytes(p) / sizeof(float);
+  return n ? c.take<float>(n) : nullptr;
+}
+
 struct ForwardWs {
   int32_t *idx, *counts, *offsets, *perm, *inv;
-  float* gate;
+  float *gate, *route_part;
   PermuteWs pw;
   FfnWs fw;
   void *x_perm, *y_perm;
@@ -89,6 +95,7 @@ ForwardWs carve_forward(Carver& c, const moe_problem_t& p) {
   w.perm = c.take<int32_t>(R);
   w.inv = c.take<int32_t>(R);
   w.pw = carve_permute(c, p);
+  w.route_part = carve_route(c, p);
   w.x_perm = c.take<char>(R * p.d_model * es);
   w.fw = carve_ffn(c, p);
   w.y_perm = c.take<char>(R * p.d_model * es);
@@ -103,6 +110,9 @@ size_t stage_bytes(const moe_problem_t& p, int32_t stage) {
       break;
     case MOE_STAGE_GROUPED_FFN:
       carve_ffn(c, p);
+      break;
+    case MOE_STAGE_ROUTE:
+      carve_route(c, p);
       break;
     default:
       carve_forward(c, p);
@@ -127,7 +137,8 @@ MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, s
   const moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
-  if (stage != MOE_STAGE_PERMUTE && stage != MOE_STAGE_GROUPED_FFN && stage != MOE_STAGE_FORWARD)
+  if (stage != MOE_STAGE_PERMUTE && stage != MOE_STAGE_GROUPED_FFN && stage != MOE_STAGE_FORWARD &&
+      stage != MOE_STAGE_ROUTE)
     return MOE_ERR_INVALID_ARGUMENT;
   *bytes = stage_bytes(*p, stage);
   return MOE_OK;
@@ -142,7 +153,23 @@ MOE_API moe_status_t moe_route(const moe_problem_t* p, const void* x, const void
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
       (router_bias && !aligned16(router_bias)) || (logits && !aligned16(logits)))
     return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(moe::launch_route(*p, x, w_router, router_bias, logits, topk_idx, topk_gate,
+  return hip_status(moe::launch_route(*p, x, w_router, router_bias, logits, topk_idx, topk_gate, nullptr,
+                                      (hipStream_t)stream));
+}
+
+MOE_API moe_status_t moe_route_ws(const moe_problem_t* p, const void* x, const void* w_router,
+                                  const float* router_bias, float* logits, int32_t* topk_idx, float* topk_gate,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_idx || !topk_gate || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_gate) || !aligned16(ws) ||
+      (router_bias && !aligned16(router_bias)) || (logits && !aligned16(logits)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_ROUTE)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  float* part = carve_route(c, *p);
+  return hip_status(moe::launch_route(*p, x, w_router, router_bias, logits, topk_idx, topk_gate, part,
                                       (hipStream_t)stream));
 }
 
@@ -247,9 +274,21 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
   const ForwardWs w = carve_forward(c, *p);
   hipStream_t s = (hipStream_t)stream;
   const int64_t R = p->T * p->k;
-  hipError_t e = moe::launch_route(*p, x, w_router, router_bias, nullptr, w.idx, w.gate, s);
-  if (e == hipSuccess)
-    e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts, w.pw.blockbase, s);
+  hipError_t e;
+  if (moe::route_permute_fused(*p)) {
+    // decode-sized batch: router partial logits, then one workgroup completes
+    // the routing and permutes (the same results as the two stages)
+    e = moe::launch_route_partials(*p, x, w_router, w.route_part, s);
+    if (e == hipSuccess)
+      e = moe::launch_finalize_permute_small(*p, w.route_part, moe::route_splits(*p), router_bias, w.idx, w.gate,
+                                             w.counts,
+                                             w.offsets, w.perm, w.inv, s);
+  } else {
+    e = moe::launch_route(*p, x, w_router, router_bias, nullptr, w.idx, w.gate, w.route_part, s);
+    if (e == hipSuccess)
+      e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts,
+                                    w.pw.blockbase, s);
+  }
   if (gather_supported(*p)) {
     // dispatch folded into the first GEMM: its A rows are read as x[perm[r]]
     if (e == hipSuccess)

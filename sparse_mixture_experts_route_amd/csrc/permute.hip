@@ -15,8 +15,16 @@
 //           number of tokens before t in the block that selected e (popcount
 //           of the mask below t), so rows follow token order inside a group.
 //   gather  token-major: each x row is read once and written to its k rows.
+//
+// Batches of at most kSmallPermuteT tokens (decode-sized) run the same
+// counting sort in one workgroup (permute_small_kernel): one launch instead
+// of three, each a few microseconds of mostly launch and memory latency. Its
+// FIN form first completes a router split over d_model (partial logits summed
+// in split order, then the per-token selection), so that a decode-sized layer
+// goes from the router's partial logits to perm and inv in one launch.
 #include "common.h"
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -108,6 +116,89 @@ __global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
+constexpr int kSmallWords = kSmallPermuteT / 32;  // mask words per expert
+constexpr int kSmallThreads = 1024;
+static_assert(kSmallPermuteT <= kSmallThreads, "one token per thread");
+static_assert(kFusedRouteT <= kSmallThreads / kWave, "one token per wave");
+
+// One workgroup, T <= kSmallPermuteT tokens (thread t owns token t), k <= 8.
+// FIN (T <= kFusedRouteT, one token per wave): the routing of the batch is
+// completed first, as the router's own finalize launch does it
+// (sum_partial_logits, then select_topk), so idx and gates are bitwise the
+// same; idx stays in LDS until the end, gates go out directly. Otherwise idx is read
+// from idx_in. Then the counting sort of the header: token bit masks per
+// expert, counts and offsets from popcounts and a scan, rows in token order
+// inside each group.
+template <bool FIN>
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ idx_in, const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
+    float* __restrict__ gate, int32_t* __restrict__ idx_out, int T, int k, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ uint32_t mask[256][kSmallWords];
+  __shared__ int32_t s_idx[kSmallPermuteT * 8];
+  __shared__ float lg[FIN ? kFusedRouteT : 1][256];
+  __shared__ int32_t s_scan[256];
+  __shared__ int32_t s_off[256];
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const int P = T * k;
+  const int words = (T + 31) / 32;
+  uint32_t* flat = &mask[0][0];
+  for (int i = tid; i < E * kSmallWords; i += kSmallThreads) flat[i] = 0u;
+  if constexpr (FIN) {
+    if (wave < T) {  // T <= kFusedRouteT = the workgroup's waves: one token each
+      sum_partial_logits(part, nsplit, bias, T, E, wave, lg[wave]);
+      select_topk(lg[wave], E, k, wave, nullptr, s_idx, gate);
+    }
+  } else {
+    for (int i = tid; i < P; i += kSmallThreads) s_idx[i] = idx_in[i];
+  }
+  __syncthreads();
+  if (tid < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = s_idx[tid * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr(&mask[e][tid >> 5], 1u << (tid & 31));
+    }
+  __syncthreads();
+  // counts per expert, then an inclusive scan over the 256 expert slots
+  int32_t c = 0;
+  if (tid < 256) {
+    if (tid < E)
+      for (int w = 0; w < words; ++w) c += __popc(mask[tid][w]);
+    s_scan[tid] = c;
+  }
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t v = tid < 256 && tid >= o ? s_scan[tid - o] : 0;
+    __syncthreads();
+    if (tid < 256) s_scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    s_off[tid] = s_scan[tid] - c;
+    counts[tid] = c;
+    offsets[tid] = s_scan[tid] - c;
+    if (tid == E - 1) offsets[E] = s_scan[tid];
+  }
+  __syncthreads();
+  if (tid < T) {
+    const int w = tid >> 5;
+    const uint32_t below = (1u << (tid & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+      const int e = s_idx[tid * k + j];
+      int32_t r = -1;
+      if ((unsigned)e < (unsigned)E) {
+        int rank = __popc(mask[e][w] & below);
+        for (int w2 = 0; w2 < w; ++w2) rank += __popc(mask[e][w2]);
+        r = s_off[e] + rank;
+        perm[r] = tid;
+      }
+      inv[tid * k + j] = r;
+    }
+  }
+  if constexpr (FIN)
+    for (int i = tid; i < P; i += kSmallThreads) idx_out[i] = s_idx[i];
+}
+
 // One wave per token: the row is read once in 16-byte pieces and written to
 // each of the token's k rows.
 constexpr int kGatherWaves = 4;
@@ -157,9 +248,19 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(const u32x
 
 }  // namespace
 
+bool route_permute_fused(const moe_problem_t& p) {
+  const int ns = route_splits(p);
+  return ns > 1 && p.T <= kFusedRouteT && p.k <= 8 && (int64_t)ns * p.T * p.E * 4 <= 256 * 1024;
+}
+
 hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* inv, int32_t* blockcounts, int32_t* blockbase,
                                 hipStream_t s) {
+  if (p.T <= kSmallPermuteT && p.k <= 8) {
+    hipLaunchKernelGGL(permute_small_kernel<false>, dim3(1), dim3(kSmallThreads), 0, s, idx, nullptr, 0, nullptr,
+                       nullptr, nullptr, (int)p.T, p.k, p.E, counts, offsets, perm, inv);
+    return hipGetLastError();
+  }
   const int64_t nb = permute_blocks(p.T);
   hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts);
   hipError_t err = hipGetLastError();
@@ -169,6 +270,15 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockbase, perm,
                      inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_permute_small(const moe_problem_t& p, const float* part, int nsplit, const float* bias,
+                                        int32_t* idx, float* gate, int32_t* counts, int32_t* offsets,
+                                        int32_t* perm, int32_t* inv, hipStream_t s) {
+  if (p.T > kFusedRouteT || p.k > 8 || p.E % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_small_kernel<true>, dim3(1), dim3(kSmallThreads), 0, s, nullptr, part, nsplit, bias,
+                     gate, idx, (int)p.T, p.k, p.E, counts, offsets, perm, inv);
   return hipGetLastError();
 }
 

@@ -27,108 +27,11 @@
 #include "common.h"
 #include "internal.h"
 #include "lds_dma.h"
+#include "topk.h"
 
 namespace moe {
 
 namespace {
-
-// Softmax statistics and top-k of one token whose E logits are in LDS (`lg`).
-__device__ __forceinline__ void select_topk(const float* lg, int E, int k, int64_t t, float* __restrict__ logits,
-                                            int32_t* __restrict__ idx, float* __restrict__ gate) {
-  const int lane = threadIdx.x % kWave;
-  float m = -INFINITY;
-  for (int e = lane; e < E; e += kWave) m = fmaxf(m, lg[e]);
-  m = wave_max(m);
-  float ssum = 0.0f;
-  for (int e = lane; e < E; e += kWave) ssum += expf(lg[e] - m);
-  ssum = wave_sum(ssum);
-  if (logits) {
-    for (int e = lane; e < E; e += kWave) logits[t * E + e] = lg[e];
-  }
-  uint32_t taken = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !((taken >> i) & 1u)) {
-        const uint64_t key = ((uint64_t)float_order_key(lg[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-        best = key > best ? key : best;
-      }
-    }
-    best = wave_max_u64(best);
-    const int es = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if ((es & (kWave - 1)) == lane) taken |= 1u << (es / kWave);
-    if (lane == 0) {
-      idx[t * k + j] = es;
-      gate[t * k + j] = expf(lg[es] - m) / ssum;
-    }
-  }
-}
-
-// Top-k (k <= kTopkFast) of the RT tokens of a block whose logits are in LDS
-// (row r at lg + r * ld): four threads per token, thread q of the group scans
-// experts q, q + 4, ... keeping the kTopkFast largest 64-bit keys (the keys of
-// select_topk: order-preserving logit bits above the inverted expert index,
-// all distinct) in a sorted register list; the four lists are merged over two
-// rounds of lane exchanges, so the result equals select_topk's selection.
-// Softmax maximum and sum are combined the same way (fixed order).
-constexpr int kTopkFast = 8;
-
-__device__ __forceinline__ void insert_key(uint64_t (&top)[kTopkFast], uint64_t v) {
-#pragma unroll
-  for (int j = 0; j < kTopkFast; ++j) {
-    const uint64_t hi = top[j] > v ? top[j] : v;
-    v = top[j] > v ? v : top[j];
-    top[j] = hi;
-  }
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-template <int RT_>
-__device__ __forceinline__ void select_topk_block(const float* lg, int ld, int64_t t0, int64_t T, int E, int k,
-                                                  int32_t* __restrict__ idx, float* __restrict__ gate) {
-  static_assert(RT_ * 4 == 256, "four threads per token, 256 threads");
-  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const float* row = lg + r * ld;
-  uint64_t top[kTopkFast];
-#pragma unroll
-  for (int j = 0; j < kTopkFast; ++j) top[j] = 0;  // below every finite logit's key
-  float m = -INFINITY;
-  for (int e = q; e < E; e += 4) {
-    const float l = row[e];
-    m = fmaxf(m, l);
-    insert_key(top, ((uint64_t)float_order_key(l) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e));
-  }
-  m = fmaxf(m, __shfl_xor(m, 1, kWave));
-  m = fmaxf(m, __shfl_xor(m, 2, kWave));
-  float ssum = 0.0f;
-  for (int e = q; e < E; e += 4) ssum += expf(row[e] - m);
-  ssum += __shfl_xor(ssum, 1, kWave);
-  ssum += __shfl_xor(ssum, 2, kWave);
-#pragma unroll
-  for (int o = 1; o <= 2; o <<= 1) {
-    uint64_t other[kTopkFast];
-#pragma unroll
-    for (int j = 0; j < kTopkFast; ++j) other[j] = shfl_xor_u64(top[j], o);
-#pragma unroll
-    for (int j = 0; j < kTopkFast; ++j) insert_key(top, other[j]);
-  }
-  const int64_t t = t0 + r;
-  if (q == 0 && t < T) {
-#pragma unroll
-    for (int j = 0; j < kTopkFast; ++j)
-      if (j < k) {
-        const int es = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
-        idx[t * k + j] = es;
-        gate[t * k + j] = expf(row[es] - m) / ssum;
-      }
-  }
-}
 
 // ---------------------------------------------------------------- matrix-core path
 
@@ -142,12 +45,17 @@ constexpr int RBK = 64; // K step
 // barrier per K step, the fragments of the next K sub-step read while the
 // MFMAs of the current one run. After the last step the ring holds the
 // block's float32 logits (+ bias) for the selection epilogue.
+//
+// Split over d_model (gridDim.y = nsplit > 1): block (b, s) takes K steps
+// [s nk / nsplit, (s+1) nk / nsplit) and writes its float32 partial logits
+// (no bias) to part[s][t][e]; route_finalize_kernel adds them up and selects.
 template <int EP, int S>
 __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __restrict__ x,
                                                          const bf16_bits* __restrict__ wr,
                                                          const float* __restrict__ bias, float* __restrict__ logits,
                                                          int32_t* __restrict__ idx, float* __restrict__ gate,
-                                                         int64_t T, int d, int E_real, int k) {
+                                                         float* __restrict__ part, int64_t T, int d, int E_real,
+                                                         int k) {
   constexpr int NW = 4;
   constexpr int WTN = EP / 2, TN = WTN / 32;  // experts per wave, 32-wide MFMA tiles
   constexpr int KS = RBK / 16;                // MFMA K sub-steps per stage
@@ -168,7 +76,10 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
   const int wm0 = (wave >> 1) * 32, wn0 = (wave & 1) * WTN;
   lds_char* const lds = (lds_char*)smem;
   const uint32_t lds_base = lds_addr(smem);
-  const int nk = d / RBK;
+  const int nk_all = d / RBK;
+  const int nsplit = gridDim.y, split = blockIdx.y;
+  const int kt0 = (int)((int64_t)nk_all * split / nsplit);
+  const int nk = (int)((int64_t)nk_all * (split + 1) / nsplit) - kt0;  // >= 1: nsplit <= nk_all
 
   // tokens past T and k past d read as zero (descriptor ranges)
   const int rows = (int)min((int64_t)RT, T - t0);
@@ -195,9 +106,9 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
   auto issue_one = [&](int kt, int buf, int i) {
     const uint32_t st = lds_base + buf * STAGE;
     if (i < A_LD)
-      buffer_load_lds16(rsA, a_off[i], (uint32_t)kt * RBK * 2, st + (wave * A_LD + i) * 1024);
+      buffer_load_lds16(rsA, a_off[i], (uint32_t)(kt0 + kt) * RBK * 2, st + (wave * A_LD + i) * 1024);
     else
-      buffer_load_lds16(rsB, b_off[i - A_LD], (uint32_t)kt * RBK * E_real * 2,
+      buffer_load_lds16(rsB, b_off[i - A_LD], (uint32_t)(kt0 + kt) * RBK * E_real * 2,
                         st + A_STAGE + (wave * B_LD + i - A_LD) * 1024);
   };
 
@@ -281,9 +192,18 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int e = wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5) + qq;
-        if (e < E_real) lg[(wm0 + (lane & 31)) * LG_ROW + e] = acc[ni][4 * gq + qq] + (bias ? bias[e] : 0.0f);
+        if (e < E_real)
+          lg[(wm0 + (lane & 31)) * LG_ROW + e] = acc[ni][4 * gq + qq] + (bias && nsplit == 1 ? bias[e] : 0.0f);
       }
   __syncthreads();
+  if (nsplit > 1) {  // partial logits of this K range, rows of the block, coalesced
+    float* const dst = part + ((int64_t)split * T + t0) * E_real;
+    for (int i = tid; i < rows * E_real; i += NW * kWave) {
+      const int r = i / E_real, e = i - r * E_real;
+      dst[i] = lg[r * LG_ROW + e];
+    }
+    return;
+  }
   if (k <= kTopkFast) {
     select_topk_block<RT>(lg, LG_ROW, t0, T, E_real, k, idx, gate);
     if (logits)  // rows of the block, coalesced
@@ -297,6 +217,24 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
       if (t < T) select_topk(lg + r * LG_ROW, E_real, k, t, logits, idx, gate);
     }
   }
+}
+
+// Completion of a router split over d_model, one wave per token: the token's
+// partial logits are added in split order (sum_partial_logits) and the row
+// goes to select_topk through the wave's LDS row. No block-wide barrier:
+// waves past T leave at once.
+constexpr int kFinalizeWaves = 4;
+
+__global__ __launch_bounds__(kFinalizeWaves * kWave) void route_finalize_kernel(
+    const float* __restrict__ part, int nsplit, const float* __restrict__ bias, float* __restrict__ logits,
+    int32_t* __restrict__ idx, float* __restrict__ gate, int64_t T, int E, int k) {
+  __shared__ float lg[kFinalizeWaves][256];
+  const int wave = threadIdx.x / kWave;
+  const int64_t t = (int64_t)blockIdx.x * kFinalizeWaves + wave;
+  if (t >= T) return;
+  sum_partial_logits(part, nsplit, bias, T, E, t, lg[wave]);
+  // LDS accesses of one wave execute in order: the row is complete for the reads below
+  select_topk(lg[wave], E, k, t, logits, idx, gate);
 }
 
 // ---------------------------------------------------------------- FMA path
@@ -380,16 +318,66 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_fma_kernel(
 
 }  // namespace
 
+int route_splits(const moe_problem_t& p) {
+  if (p.dtype != MOE_DTYPE_BF16 || p.E % 8 != 0) return 1;
+  const int64_t blocks = ceil_div(p.T, RT);
+  const int cus = device_cus();
+  // measured on MI355X: with a quarter of the CUs or more busy the single pass
+  // (contraction and selection in one launch) is faster than a split plus the
+  // wave-per-token finalize (e.g. 8192 tokens, 64 experts, top-8: 27 against 32 us)
+  if (blocks * 4 > cus) return 1;
+  const int nk = p.d_model / RBK;
+  int64_t ns = ceil_div(2 * cus, blocks);  // about two router blocks per CU
+  ns = min(ns, (int64_t)nk / 4);           // at least four K steps per split
+  // partial logits that one finalize wave adds up for its token: at most 64 KB
+  ns = min(ns, (int64_t)(64 * 1024) / (p.E * 4));
+  return (int)max(ns, (int64_t)1);
+}
+
+size_t route_partials_bytes(const moe_problem_t& p) {
+  const int ns = route_splits(p);
+  return ns > 1 ? (size_t)ns * p.T * p.E * sizeof(float) : 0;
+}
+
+hipError_t launch_route_partials(const moe_problem_t& p, const void* x, const void* w_router, float* part,
+                                 hipStream_t s) {
+  const int ns = route_splits(p);
+  if (ns <= 1 || !part) return hipErrorInvalidValue;
+  const int64_t blocks = ceil_div(p.T, RT);
+  const bf16_bits* xb = (const bf16_bits*)x;
+  const bf16_bits* wb = (const bf16_bits*)w_router;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ns), dim3(256), 0, s, xb, wb, nullptr, nullptr,
+                       nullptr, nullptr, part, p.T, p.d_model, p.E, p.k);
+    return hipGetLastError();
+  };
+  switch ((p.E + 63) / 64 * 64) {
+    case 64:
+      return go(route_mfma_kernel<64, 4>);
+    case 128:
+      return go(route_mfma_kernel<128, 4>);
+    case 192:
+      return go(route_mfma_kernel<192, 3>);
+    default:
+      return go(route_mfma_kernel<256, 3>);
+  }
+}
+
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* w_router, const float* bias,
-                        float* logits, int32_t* idx, float* gate, hipStream_t s) {
+                        float* logits, int32_t* idx, float* gate, float* part, hipStream_t s) {
   if (p.dtype == MOE_DTYPE_BF16 && p.E % 8 == 0) {
     const int64_t blocks = ceil_div(p.T, RT);
     const bf16_bits* xb = (const bf16_bits*)x;
     const bf16_bits* wb = (const bf16_bits*)w_router;
     const int ep = (p.E + 63) / 64 * 64;  // padded expert count
+    const int ns = part ? route_splits(p) : 1;
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, xb, wb, bias, logits, idx, gate, p.T,
-                         p.d_model, p.E, p.k);
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ns), dim3(256), 0, s, xb, wb, bias, logits, idx,
+                         gate, part, p.T, p.d_model, p.E, p.k);
+      if (ns > 1)
+        hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)ceil_div(p.T, kFinalizeWaves)),
+                           dim3(kFinalizeWaves * kWave), 0, s,
+                           (const float*)part, ns, bias, logits, idx, gate, p.T, p.E, p.k);
       return hipGetLastError();
     };
     // ring stages: 4 while a stage is small, 3 for the widest tiles (LDS: S * (8 KB + 128 * EP B))

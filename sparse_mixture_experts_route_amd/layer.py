@@ -31,7 +31,10 @@ class MoEForward:
         return self.y
 
     def stages(self, x, w_router, W1, W2, router_bias=None, stream=None, logits=True):
-        """Run the four stage entry points one after another; return every intermediate."""
+        """Run the four stage entry points one after another; return every intermediate.
+
+        Routing goes through moe_route_ws, the router moe_forward runs, so both
+        paths select on logits summed in the same order."""
         p = self.problem
         T, E, k = p.T, p.E, p.k
         R = T * k
@@ -50,7 +53,8 @@ class MoEForward:
         }
         ws_p = torch.empty(_lib.moe_workspace_size(p, _lib.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
         ws_f = torch.empty(_lib.moe_workspace_size(p, _lib.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
-        _lib.moe_route(p, x, w_router, router_bias, out["logits"], out["idx"], out["gate"], stream)
+        ws_r = torch.empty(_lib.moe_workspace_size(p, _lib.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
+        _lib.moe_route_ws(p, x, w_router, router_bias, out["logits"], out["idx"], out["gate"], ws_r, stream)
         _lib.moe_permute(p, out["idx"], x, out["counts"], out["offsets"], out["perm"], out["inv"], out["x_perm"],
                          ws_p, stream)
         _lib.moe_grouped_ffn(p, out["x_perm"], out["offsets"], W1, W2, out["y_perm"], ws_f, stream)

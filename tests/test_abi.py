@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "moe_workspace_size", "moe_route", "moe_permute", "moe_permute_index", "moe_grouped_ffn",
+        "moe_workspace_size", "moe_route", "moe_route_ws", "moe_permute", "moe_permute_index", "moe_grouped_ffn",
         "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_status_str"])
 
 
@@ -142,3 +142,22 @@ def test_permute_index_and_ffn_gather_reject_before_launch(moe, lib):
     assert lib.moe_grouped_ffn_gather(ctypes.byref(f32), A, A, A, A, A, A, A2, 1 << 40, s) == UNSUPPORTED
     big = P(moe, T=1 << 20, d=1024, k=1)
     assert lib.moe_grouped_ffn_gather(ctypes.byref(big), A, A, A, A, A, A, A2, 1 << 40, s) == UNSUPPORTED
+
+
+def test_route_ws_rejects_before_launch_and_sizes_its_partials(moe, lib):
+    p = P(moe)
+    s = ctypes.c_void_p(0)
+    assert lib.moe_route_ws(ctypes.byref(p), None, A, None, None, A, A, A2, 1 << 20, s) == INVALID
+    assert lib.moe_route_ws(ctypes.byref(p), A, A, None, None, A, A, None, 1 << 20, s) == INVALID
+    assert lib.moe_route_ws(ctypes.byref(p), A, A, None, None, A, A, MIS, 1 << 20, s) == INVALID
+    assert lib.moe_route_ws(ctypes.byref(P(moe, d=100)), A, A, None, None, A, A, A2, 1 << 20, s) == UNSUPPORTED
+    # a decode-sized bf16 batch splits the router over d_model: float32 partial
+    # logits of several splits per token; a batch that fills the GPU needs none
+    small = P(moe, T=8, d=7168, E=256, k=8, de=2048)
+    need = moe.moe_workspace_size(small, moe.MOE_STAGE_ROUTE)
+    assert need >= 2 * 8 * 256 * 4
+    assert lib.moe_route_ws(ctypes.byref(small), A, A, None, None, A, A, A2, need - 1, s) == WS_SMALL
+    big = P(moe, T=65536, d=2048, E=64, k=8, de=1024)
+    assert moe.moe_workspace_size(big, moe.MOE_STAGE_ROUTE) <= 256
+    f32 = P(moe, T=8, d=2048, E=8, k=2, de=256, dtype=0)
+    assert moe.moe_workspace_size(f32, moe.MOE_STAGE_ROUTE) <= 256

@@ -58,7 +58,8 @@ def test_grouped_ffn_against_oracle(moe, R, d, de, E, dtype, empty):
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x256k32", "256x128", "128x128", "128x128k32", "256x256w8", "256x256w8k32"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256k32", "256x128", "128x128", "128x128k32", "256x256w8", "256x256w8k32",
+                                  "32x256"])
 def test_every_tile_shape(moe, tile):
     """Each bf16 block tile the launcher can choose, on ragged groups with
     empty experts and rows that are not a multiple of any tile."""
@@ -78,7 +79,7 @@ def test_every_tile_shape(moe, tile):
 
 
 @pytest.mark.parametrize("blocks", [24, 64])
-@pytest.mark.parametrize("tile", ["256x256w8", "128x128", "256x128"])
+@pytest.mark.parametrize("tile", ["256x256w8", "128x128", "256x128", "32x256"])
 @pytest.mark.parametrize("R,d,de,E", [(20000, 128, 64, 3), (9000, 512, 64, 2), (6000, 256, 192, 7)])
 def test_split_leftover_tiles(moe, tile, R, d, de, E, blocks):
     """A capped persistent grid gives several rounds of tiles and a small
@@ -116,7 +117,8 @@ def test_rows_past_offsets_end_untouched(moe):
 
 
 @pytest.mark.parametrize("tile,split0", [("auto", False), ("256x256w8", True), ("128x128", False),
-                                         ("256x128", True), ("256x256w8k32", False)])
+                                         ("256x128", True), ("256x256w8k32", False), ("32x256", True),
+                                         ("32x256", False)])
 def test_gather_path_matches_permuted_copy(moe, tile, split0):
     """moe_permute_index + moe_grouped_ffn_gather (the first GEMM reads x[perm[r]])
     give the same index arrays and the same y_perm, bit for bit, as moe_permute

@@ -39,6 +39,10 @@ CASES = [
     (3001, 128, 256, 8, "bf16", (), tuple(range(100, 140))),
     (700, 64, 16, 16, "f32", (), ()),
     (300, 64, 256, 256, "bf16", (), ()),
+    # batches of at most 1024 tokens with k <= 8 run in one workgroup: its limits
+    (1024, 64, 256, 8, "bf16", (5,), tuple(range(200, 256))),
+    (1025, 64, 256, 8, "bf16", (5,), ()),
+    (64, 64, 8, 1, "bf16", (), (7,)),
 ]
 
 

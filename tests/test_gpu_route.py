@@ -12,31 +12,39 @@ from harness.configs import CONFIG_ORDER
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def run_route(moe, cfg, x, wr, bias):
+def run_route(moe, cfg, x, wr, bias, via="moe_route"):
+    """Route through moe_route, or through moe_route_ws (which splits the
+    contraction over d_model when the tokens alone do not fill the GPU)."""
     p = moe.make_problem(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, cfg.dtype)
     dev = x.device
     logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
-    moe.moe_route(p, x, wr, bias, logits, idx, gate)
+    if via == "moe_route":
+        call = lambda lg, i, g: moe.moe_route(p, x, wr, bias, lg, i, g)  # noqa: E731
+    else:
+        ws = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
+        call = lambda lg, i, g: moe.moe_route_ws(p, x, wr, bias, lg, i, g, ws)  # noqa: E731
+    call(logits, idx, gate)
     # the same routing without exporting logits
     idx2 = torch.empty_like(idx)
     gate2 = torch.empty_like(gate)
-    moe.moe_route(p, x, wr, bias, None, idx2, gate2)
+    call(None, idx2, gate2)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(gate, gate2)
     return f64(logits).astype(np.float32), i64(idx), f64(gate)
 
 
+@pytest.mark.parametrize("via", ["moe_route", "moe_route_ws"])
 @pytest.mark.parametrize("name", CONFIG_ORDER)
-def test_route_full_size_against_oracle(moe, name):
+def test_route_full_size_against_oracle(moe, name, via):
     """Every workload at full size: logits within the float32 rounding bound,
     selected sets equal outside near-ties, gates within the bound implied by
     the logit difference, and idx exactly the top-k of the GPU's own logits."""
     cfg = CONFIGS[name]
-    announce(f"route full {name} T={cfg.T} d={cfg.d_model} E={cfg.E} k={cfg.k}")
+    announce(f"route full {name} via {via} T={cfg.T} d={cfg.d_model} E={cfg.E} k={cfg.k}")
     inp = make_inputs(cfg, seed=0, device="cuda", weights=False)
-    logits, idx, gate = run_route(moe, cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    logits, idx, gate = run_route(moe, cfg, inp["x"], inp["w_router"], inp["router_bias"], via)
     xh, wh, bh = host_array(inp["x"]), host_array(inp["w_router"]), host_array(inp["router_bias"])
     x64, w64 = oracle.decode(xh, cfg.dtype), oracle.decode(wh, cfg.dtype)
     ref = oracle.route(x64, w64, bh, cfg.k)
@@ -64,22 +72,27 @@ def test_route_full_size_against_oracle(moe, name):
     assert np.all(rel[ok] <= np.broadcast_to(tol, rel.shape)[ok]), f"gate error {rel[ok].max():.3e}"
 
 
+@pytest.mark.parametrize("via", ["moe_route", "moe_route_ws"])
 @pytest.mark.parametrize("tie_group", [1, 3])
 @pytest.mark.parametrize("name,T,d,bias", [
     ("tiny_fp32", 200, 128, False),
     ("mixtral_coarse", 333, 2048, False),
     ("fine_grained", 517, 2048, True),
     ("large_sparse", 130, 7168, True),
+    # decode-sized batches: moe_route_ws splits these over d_model
+    ("mixtral_coarse", 1, 2048, False),
+    ("large_sparse", 8, 7168, True),
+    ("fine_grained", 64, 1024, True),
 ])
-def test_route_bit_exact_on_exact_logits(moe, name, T, d, bias, tie_group):
+def test_route_bit_exact_on_exact_logits(moe, name, T, d, bias, tie_group, via):
     """Inputs whose float32 logits are exact in any summation order: logits and
     indices must be bit-exact, gates within the float32 softmax rounding bound.
     With tie_group=3 experts tie in threes, so the lowest-index rule decides
     the k-th place of every token."""
     cfg = scaled_config(name, T=T, d_model=d)
-    announce(f"route exact {cfg.name} T={T} d={d} E={cfg.E} k={cfg.k} bias={bias} ties={tie_group}")
+    announce(f"route exact {cfg.name} via {via} T={T} d={d} E={cfg.E} k={cfg.k} bias={bias} ties={tie_group}")
     inp = make_exact_router_inputs(cfg, seed=1, device="cuda", bias=bias, tie_group=tie_group)
-    logits, idx, gate = run_route(moe, cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    logits, idx, gate = run_route(moe, cfg, inp["x"], inp["w_router"], inp["router_bias"], via)
     bh = host_array(inp["router_bias"])
     ref = oracle.route(oracle.decode(host_array(inp["x"]), cfg.dtype),
                        oracle.decode(host_array(inp["w_router"]), cfg.dtype), bh, cfg.k)
@@ -90,7 +103,7 @@ def test_route_bit_exact_on_exact_logits(moe, name, T, d, bias, tie_group):
     s = -np.sort(-ref["logits"], axis=1)
     n_ties = int(np.sum(s[:, cfg.k - 1] == s[:, cfg.k])) if cfg.k < cfg.E else 0
     print(f"{cfg.name}: {n_ties} tokens with a tie at the k-th place")
-    if tie_group > 1:
+    if tie_group > 1 and cfg.k < cfg.E:
         assert n_ties > cfg.T // 4
 
 
