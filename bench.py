@@ -27,19 +27,22 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def algorithmic_bytes(cfg, gather):
+def algorithmic_bytes(cfg, gather, used_experts=None):
     """Bytes each phase must move at minimum (inputs read once, outputs written once).
 
     With `gather` the permute phase only builds the index arrays and the FFN
-    phase reads the token rows from x itself (no permuted copy)."""
+    phase reads the token rows from x itself (no permuted copy). The FFN reads
+    the weights of the experts that received tokens (`used_experts`, all E when
+    not given)."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k, de = cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert
+    Eu = E if used_experts is None else used_experts
     R = T * k
     a_in = T * d * es if gather else R * d * es
     return {
         "route": T * d * es + d * E * es + R * 8,
         "permute": R * 4 + R * 8 + (0 if gather else T * d * es + R * d * es),
-        "ffn": a_in + 2 * E * d * de * es + 2 * R * de * es + R * d * es,
+        "ffn": a_in + 2 * Eu * d * de * es + 2 * R * de * es + R * d * es,
         "combine": R * d * es + R * 8 + T * d * es,
     }
 
@@ -118,6 +121,9 @@ def main():
     ap.add_argument("--config", default="mixtral_coarse",
                     help="workload: tiny_fp32, mixtral_coarse, fine_grained, skewed, large_sparse")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch size T instead of the workload's (e.g. 1..160 for decode-sized batches)")
+    ap.add_argument("--k", type=int, default=0, help="experts per token instead of the workload's")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -134,9 +140,11 @@ def main():
     import torch
     ensure_built()
     import sparse_mixture_experts_route_amd as moe
-    from harness import CONFIGS, make_inputs
+    from harness import CONFIGS, make_inputs, scaled_config
 
     cfg = CONFIGS[args.config]
+    if args.tokens or args.k:
+        cfg = scaled_config(args.config, T=args.tokens or None, k=args.k or None, suffix=f"T{args.tokens or cfg.T}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration_mib:
@@ -215,10 +223,22 @@ def main():
     assert torch.equal(bufs["y"], layer.y), "stage path and moe_forward disagree"
 
     flops = cfg.ffn_flops()
-    bytes_ = algorithmic_bytes(cfg, gather)
+    used = int((bufs["counts"] > 0).sum().item())
+    bytes_ = algorithmic_bytes(cfg, gather, used)
     t_ffn = phase_ms["ffn"] * 1e-3
     ffn_tflops = flops / t_ffn / 1e12
-    if cfg.dtype == "bf16":
+    # the FFN phase is bound by the matrix cores when its flops per algorithmic
+    # byte exceed the chip's balance (2.5 PFLOP/s / 8 TB/s), by HBM otherwise
+    # (decode-sized batches: streaming the used experts' weights)
+    mfma_bound = flops / bytes_["ffn"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
+    if cfg.dtype == "bf16" and not mfma_bound:
+        gbs = bytes_["ffn"] / t_ffn / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel": f"grouped FFN phase: gemm_bf16_kernel x2 (32x256 weight-streaming tile) + "
+                              f"gemm_fixup_kernel x2; bytes = weights of the {used} experts with tokens "
+                              f"+ activations"}
+    elif cfg.dtype == "bf16":
         roofline = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(cfg.name),
