@@ -10,22 +10,30 @@ runs them on one GPU. Every phase time is linear in a few terms taken from
 the kernels' own work and schedule, so the constants are a least-squares fit:
 
   route     a0 + (a1 + a2 * E64 / 64) * K steps of 64 in the busiest CU's
-            chain of router blocks + a3 * M token-expert logits selected over
-            (a block scores 64 tokens against the E64 experts padded to 64;
-            most layers give every CU at most one round of such blocks, so
-            the serial chain, not HBM, sets the time)
-  permute   b0 + b1 * M selections (index arrays only: the token rows reach
-            the first GEMM through perm)
+            chain of router blocks + a3 * thousands of partial logits a
+            finalize wave adds per token (splits x E; small batches split
+            d_model) + a4 * M selections (a block scores 64 tokens against
+            the E64 experts padded to 64; most layers give every CU at most
+            one round of such blocks, so the serial chain, not HBM, sets the
+            time)
+  permute   b0 + b1 * [one-workgroup form, T <= 1024] + b2 * M selections
+            (index arrays only: the token rows reach the first GEMM through
+            perm)
   ffn       per grouped GEMM: f0 + f1 * K steps of 64 run by the busiest
-            persistent block + f2 * tiles that block runs + f3 * MB of
-            split-tile partial sums written and read back (f0 comes out
-            negative: the step count charges in full the first and last
-            steps of a tile, which the pipeline overlaps with its neighbours)
-  combine   c0 + c1 * MB read and written
+            persistent block of a matrix-core tile + f2 * tiles that block
+            runs + f3 * MB of split-tile partial sums written and read back
+            + f4 * K steps of the busiest block of the 32-row weight-streaming
+            tile (f0 comes out negative: the step count charges in full the
+            first and last steps of a tile, which the pipeline overlaps with
+            its neighbours)
+  combine   c0 + c1 * MB read and written + c2 * thousands of elements one
+            token's wave reads (k rows of d_model: the latency chain of small
+            batches)
 
-The GEMM terms replay the kernel's schedule: 256 x 256 tiles per expert
-group, dealt to 8 XCDs x (CUs / 8) persistent blocks, whole rounds first and
-a small leftover round of long tiles split over the blocks by K steps.
+The terms replay the launcher's decisions: the router split, the permute
+form, the GEMM tile per problem, tiles per expert group dealt to 8 XCDs x
+(CUs / 8) persistent blocks, whole rounds first and a leftover round of long
+tiles split over the blocks by K steps.
 
 The model covers the bf16 layer. `measure()` times the phases on the GPU
 through the library's stage entry points (the whole-layer path's own calls);
@@ -78,16 +86,22 @@ SHAPES = [
     ("256x128", 256, 128, 32, 2, 0.8), ("128x128", 128, 128, 64, 2, 0.75),
     ("128x128k32", 128, 128, 32, 2, 0.0), ("256x256w8", 256, 256, 64, 1, 1.0),
     ("256x256w8k32", 256, 256, 32, 1, 0.0),
+    ("32x256", 32, 256, 64, 1, 0.0),  # weight streaming: picked by row count, not by score
 ]
+DECODE_TILE = 7
 
 
-def _split(rem: int, nb: int, nk: int) -> bool:
-    return rem > 0 and rem * 3 <= nb and nk * (nb - rem) >= SPLIT_MIN_STEPS * nb
+def _split(rem: int, nb: int, nk: int, max_rem: Optional[int] = None) -> bool:
+    max_rem = nb // 3 if max_rem is None else max_rem
+    return 0 < rem <= max_rem and nk * (nb - rem) >= SPLIT_MIN_STEPS * nb
 
 
 def pick_tile(R: int, K: int, N: int, E: int) -> int:
-    """The launcher's tile choice: best product of tile efficiency, round
+    """The launcher's tile choice: the 32-row streaming tile for at most ~40
+    rows per expert, else the best product of tile efficiency, round
     occupancy and row-padding efficiency."""
+    if R <= 40 * E and K % 64 == 0:
+        return DECODE_TILE
     best, best_score = 5, -1.0
     for c, (_, bm, bn, bk, occ, eff) in enumerate(SHAPES):
         if eff <= 0.0 or K % bk:
@@ -109,21 +123,23 @@ def pick_tile(R: int, K: int, N: int, E: int) -> int:
 
 
 def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, float]:
-    """Work of the busiest persistent block of one grouped-GEMM launch, in
-    units of the 8-wave 256 x 256 tile: K steps of 64 (scaled by the tile's
+    """Work of the busiest persistent block of one grouped-GEMM launch: K
+    steps of 64 in units of the 8-wave 256 x 256 tile (scaled by the tile's
     MAC count, blocks sharing a CU and matrix-core efficiency), tiles begun,
-    and split partial sums moved."""
+    split partial sums moved, and K steps of the weight-streaming tile."""
     R = sum(counts)
-    _, bm, bn, bk, occ, eff = SHAPES[pick_tile(R, K, N, E)]
+    shape = pick_tile(R, K, N, E)
+    _, bm, bn, bk, occ, eff = SHAPES[shape]
+    stream = shape == DECODE_TILE
     n_t = math.ceil(N / bn)
     tiles = sum(math.ceil(c / bm) for c in counts) * n_t
     tiles_ub = ((R + E * (bm - 1)) // bm) * n_t
-    grid = max(8, min(math.ceil(tiles_ub / 8) * 8, CUS * occ))
+    grid = CUS * occ if stream else max(8, min(math.ceil(tiles_ub / 8) * 8, CUS * occ))
     nb = grid // 8
     nk = K // bk
     tx = math.ceil(tiles / 8)  # tiles of the fullest XCD (each XCD takes a contiguous eighth)
     full, rem = divmod(tx, nb)
-    if _split(rem, nb, nk):
+    if _split(rem, nb, nk, nb - 1 if stream else None):
         steps = full * nk + math.ceil(rem * nk / nb)
         n_tiles = full + 1
         partial_mb = 2 * 8 * nb * bm * bn * 4 / 1e6  # every block writes a share, the fixup reads it
@@ -131,8 +147,21 @@ def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, floa
         n_tiles = full + (1 if rem else 0)
         steps = n_tiles * nk
         partial_mb = 0.0
+    if stream:
+        return {"steps": 0.0, "tiles": n_tiles, "partial_mb": partial_mb, "stream_steps": steps}
     scale = (bm * bn * bk * occ) / (256 * 256 * 64) / eff
-    return {"steps": steps * scale, "tiles": n_tiles * occ, "partial_mb": partial_mb}
+    return {"steps": steps * scale, "tiles": n_tiles * occ, "partial_mb": partial_mb, "stream_steps": 0.0}
+
+
+def route_splits(T: int, d: int, E: int) -> int:
+    """The router's split over d_model: only when the 64-token blocks fill at
+    most a quarter of the CUs; about two blocks per CU, at least four K steps
+    per split, at most 64 KB of partial logits per token."""
+    blocks = math.ceil(T / 64)
+    if E % 8 or blocks * 4 > CUS:
+        return 1
+    ns = min(math.ceil(2 * CUS / blocks), (d // 64) // 4, 65536 // (E * 4))
+    return max(ns, 1)
 
 
 def _route_blocks_per_cu(ep: int) -> int:
@@ -150,16 +179,18 @@ def features(s: Sample) -> Dict[str, np.ndarray]:
     R = T * k
     es = 2
     ep = math.ceil(E / 64) * 64
-    rounds = math.ceil(math.ceil(T / 64) / (CUS * _route_blocks_per_cu(ep)))
-    chain = rounds * d / 64
+    ns = route_splits(T, d, E)
+    rounds = math.ceil(math.ceil(T / 64) * ns / (CUS * _route_blocks_per_cu(ep)))
+    chain = rounds * math.ceil(d / 64 / ns)
+    small = 1.0 if T <= 1024 and k <= 8 else 0.0
     g1 = _gemm_terms(s.counts, d, de, E)
     g2 = _gemm_terms(s.counts, de, d, E)
     return {
-        "route": np.array([1.0, chain, chain * ep / 64, T * E / 1e6]),
-        "permute": np.array([1.0, R / 1e6]),
+        "route": np.array([1.0, chain, chain * ep / 64, (ns * E / 1e3) if ns > 1 else 0.0, R / 1e6]),
+        "permute": np.array([1.0, small, R / 1e6]),
         "ffn": np.array([2.0, g1["steps"] + g2["steps"], g1["tiles"] + g2["tiles"],
-                         g1["partial_mb"] + g2["partial_mb"]]),
-        "combine": np.array([1.0, (R * d * es + T * d * es) / 1e6]),
+                         g1["partial_mb"] + g2["partial_mb"], g1["stream_steps"] + g2["stream_steps"]]),
+        "combine": np.array([1.0, (R * d * es + T * d * es) / 1e6, k * d / 1e3]),
     }
 
 
@@ -299,10 +330,14 @@ FIT_SHAPES = [
     (2048, 1024, 16, 2, 4096), (8192, 4096, 32, 4, 2048), (4096, 1024, 64, 8, 512),
     (16384, 1024, 8, 1, 4096), (1024, 2048, 8, 2, 8192), (8192, 2048, 128, 8, 768),
     (32768, 1024, 32, 2, 1024), (4096, 4096, 8, 2, 4096), (12288, 2048, 16, 4, 2048),
+    # decode-sized batches
+    (1, 2048, 8, 2, 8192), (32, 2048, 8, 2, 8192), (8, 2048, 64, 8, 1024), (64, 4096, 16, 2, 4096),
+    (16, 7168, 256, 8, 2048), (128, 1024, 32, 1, 2048),
 ]
 HELD_OUT_SHAPES = [
     (16384, 7168, 256, 8, 2048), (6144, 3072, 24, 3, 3072), (12288, 1536, 48, 6, 1536),
     (3072, 2048, 8, 2, 14336), (2048, 4096, 64, 4, 1024), (24576, 1024, 16, 2, 2048),
+    (4, 2048, 8, 2, 8192), (24, 3072, 24, 3, 3072), (128, 2048, 64, 8, 1024), (8, 7168, 256, 8, 2048),
 ]
 
 
