@@ -1,4 +1,4 @@
-"""CPU oracle for the sparse MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the sparse MoE layer forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package. The product path (the HIP library and its Python binding)
@@ -21,4 +21,11 @@ from .moe_oracle import (  # noqa: F401
     forward,
     forward_literal,
     forward_tokens,
+    softmax_probs,
+)
+from .moe_backward import (  # noqa: F401
+    backward,
+    backward64,
+    forward64_fixed,
+    gelu_tanh_grad,
 )

@@ -72,16 +72,20 @@ def decode(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
 # router: Linear + Softmax, top-k (blog section 3, structure)
 # ---------------------------------------------------------------------------
 
-def router_logits(x64: np.ndarray, wr64: np.ndarray, bias: Optional[np.ndarray]) -> np.ndarray:
+def router_logits(x64: np.ndarray, wr64: np.ndarray, bias: Optional[np.ndarray],
+                  rounded: bool = True) -> np.ndarray:
     """Router Linear: logits = x Wr (+ b), computed in float64 then rounded to float32.
 
     x64 [T,d], wr64 [d,E] float64; bias [E] float32 or None. Routing is defined
-    on the float32 result.
+    on the float32 result. With rounded=False the float64 logits are returned
+    (and a float64 bias is taken as is): the smooth function whose derivative
+    the backward computes.
     """
     logits64 = x64 @ wr64
     if bias is not None:
-        logits64 = logits64 + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
-    return logits64.astype(np.float32)
+        b = np.asarray(bias, dtype=np.float32) if rounded else np.asarray(bias, dtype=np.float64)
+        logits64 = logits64 + b.astype(np.float64)[None, :]
+    return logits64.astype(np.float32) if rounded else logits64
 
 
 def topk_select(logits32: np.ndarray, k: int) -> np.ndarray:
@@ -102,13 +106,17 @@ def topk_select(logits32: np.ndarray, k: int) -> np.ndarray:
     return idx
 
 
-def softmax_gates(logits32: np.ndarray, idx: np.ndarray) -> np.ndarray:
-    """Softmax over all E logits (float64, max subtracted); gate = probability of each selected expert."""
-    l64 = logits32.astype(np.float64)
+def softmax_probs(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all E logits of each token (float64, max subtracted)."""
+    l64 = logits.astype(np.float64)
     m = l64.max(axis=1, keepdims=True)
     ex = np.exp(l64 - m)
-    p = ex / ex.sum(axis=1, keepdims=True)
-    return np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def softmax_gates(logits32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Softmax over all E logits (float64, max subtracted); gate = probability of each selected expert."""
+    return np.take_along_axis(softmax_probs(logits32), idx.astype(np.int64), axis=1)
 
 
 def near_ties(logits32: np.ndarray, k: int, margin: float = 1e-6) -> np.ndarray:
