@@ -61,7 +61,8 @@ typedef enum {
   MOE_STAGE_PERMUTE = 0,
   MOE_STAGE_GROUPED_FFN = 1,
   MOE_STAGE_FORWARD = 2,
-  MOE_STAGE_ROUTE = 3
+  MOE_STAGE_ROUTE = 3,
+  MOE_STAGE_TRAIN = 4
 } moe_stage_t;
 
 typedef struct {
@@ -74,7 +75,8 @@ typedef struct {
 } moe_problem_t;
 
 /* Workspace bytes that `stage` needs for problem `p` (host only, no HIP call).
- * moe_route and moe_combine need none; moe_route_ws takes MOE_STAGE_ROUTE. */
+ * moe_route and moe_combine need none; moe_route_ws takes MOE_STAGE_ROUTE;
+ * moe_forward_train and moe_backward share one MOE_STAGE_TRAIN workspace. */
 moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes);
 
 /* Router Linear + Softmax + top-k (blog section 3, structure: the gating
@@ -169,6 +171,38 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
                          const float* router_bias, const void* W1, const void* W2, void* y,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Training forward: moe_forward's result, and in ws what moe_backward needs
+ * (router logits, routing, permutation, U = x W1 per expert row, H =
+ * GELU_tanh(U), the expert outputs). H is GELU_tanh of the bf16-rounded U,
+ * so y can differ from moe_forward's (which rounds once, after GELU) in the
+ * last bits. bf16 only, k <= 8, E a multiple of 8, x under 2 GiB;
+ * otherwise MOE_ERR_UNSUPPORTED.
+ *   ws at least moe_workspace_size(p, MOE_STAGE_TRAIN) bytes; the caller keeps
+ *   it untouched until the matching moe_backward call has been enqueued */
+moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void* w_router,
+                               const float* router_bias, const void* W1, const void* W2, void* y,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Layer backward for the last moe_forward_train call on the same ws (same p,
+ * x, w_router, W1, W2), given dy = dL/dy: the chain rule of the layer of blog
+ * section 3 (y = sum over the selected experts of gate * expert output), with
+ * no gradient through the choice of experts:
+ *   dx [T, d_model] bf16           input gradient (expert paths + router path)
+ *   dw_router [d_model, E] bf16    router weight gradient
+ *   dbias [E] float32 or NULL      router bias gradient (sum over tokens of dlogit)
+ *   dW1 [E, d_model, d_expert], dW2 [E, d_expert, d_model] bf16
+ *                                  expert weight gradients (zero for experts without tokens)
+ *   load_frac [E] float32 or NULL  share of the T*k selections per expert
+ *   mean_prob [E] float32 or NULL  mean router probability per expert
+ * The last two are the ingredients of a load-balancing loss, whose formula
+ * the pages do not give. Products accumulate in float32; the intermediates
+ * (dYp, dU, dX, router logit gradients) are rounded to bf16 between GEMMs. */
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_router,
+                          const void* W1, const void* W2, const void* dy, void* dx,
+                          void* dw_router, float* dbias, void* dW1, void* dW2,
+                          float* load_frac, float* mean_prob, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_str(int32_t status);

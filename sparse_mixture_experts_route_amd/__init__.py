@@ -14,12 +14,15 @@ from ._lib import (  # noqa: F401
     MOE_STAGE_GROUPED_FFN,
     MOE_STAGE_PERMUTE,
     MOE_STAGE_ROUTE,
+    MOE_STAGE_TRAIN,
     MoEError,
     Problem,
     lib_path,
     make_problem,
     moe_combine,
+    moe_backward,
     moe_forward,
+    moe_forward_train,
     moe_grouped_ffn,
     moe_grouped_ffn_gather,
     moe_permute,

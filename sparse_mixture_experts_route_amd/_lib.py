@@ -18,6 +18,7 @@ MOE_STAGE_PERMUTE = 0
 MOE_STAGE_GROUPED_FFN = 1
 MOE_STAGE_FORWARD = 2
 MOE_STAGE_ROUTE = 3
+MOE_STAGE_TRAIN = 4
 
 
 class MoEError(RuntimeError):
@@ -47,6 +48,8 @@ def _load():
         "moe_grouped_ffn_gather": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [P, vp, vp, vp, vp, vp],
         "moe_forward": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_forward_train": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_backward": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -150,6 +153,19 @@ def moe_combine(p: Problem, y_perm, inv, topk_gate, y, stream=None):
 def moe_forward(p: Problem, x, w_router, router_bias, W1, W2, y, ws, stream=None):
     _check(_lib.moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(W1), _ptr(W2),
                             _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_train(p: Problem, x, w_router, router_bias, W1, W2, y, ws, stream=None):
+    _check(_lib.moe_forward_train(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(W1), _ptr(W2),
+                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward_train")
+
+
+def moe_backward(p: Problem, x, w_router, W1, W2, dy, dx, dw_router, dbias, dW1, dW2, load_frac, mean_prob, ws,
+                 stream=None):
+    _check(_lib.moe_backward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(W1), _ptr(W2), _ptr(dy), _ptr(dx),
+                             _ptr(dw_router), _ptr(dbias), _ptr(dW1), _ptr(dW2), _ptr(load_frac), _ptr(mean_prob),
+                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_backward")
 
 
 def raw_lib():

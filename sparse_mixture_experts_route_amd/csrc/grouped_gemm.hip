@@ -52,6 +52,7 @@
 #include "common.h"
 #include "internal.h"
 #include "lds_dma.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -101,46 +102,6 @@ __device__ __forceinline__ void find_tile(const int32_t* __restrict__ offsets, i
       }
     }
     if (who == 0 && lane == 0) info[0] = -1;
-  }
-  __syncthreads();
-}
-
-// Tile list of the bf16 path: tstart[e] = first tile of expert e (exclusive
-// prefix over experts of m_tiles(e) * n_tiles), tstart[E] = total;
-// mtiles[e] = ceil(rows_e / BM). Computed by wave 0, shared through LDS.
-template <int BM>
-__device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets, int E, int64_t R,
-                                                int n_tiles, int* tstart, int* mtiles) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int cnt[4];
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      int c = 0;
-      if (e < E) {
-        const int64_t lo = max((int64_t)offsets[e], (int64_t)0), hi = min((int64_t)offsets[e + 1], R);
-        c = hi > lo ? (int)ceil_div(hi - lo, BM) : 0;
-        mtiles[e] = c;
-      }
-      cnt[i] = c * n_tiles;
-      local += cnt[i];
-    }
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += v;
-    }
-    int run = incl - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      if (e < E) tstart[e] = run;
-      run += cnt[i];
-    }
-    if (lane == kWave - 1) tstart[E] = incl;
   }
   __syncthreads();
 }
@@ -977,6 +938,13 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
+  } else if (perm) {  // the first GEMM without its activation (training keeps U = x W1)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false, true>), dim3((unsigned)grid), dim3(NT),
+                       0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
+                       n_tiles, min_steps, max_rem, perm, a_rows);
+    if (fix_grid)
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else if (gelu) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
@@ -1050,8 +1018,8 @@ size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
                                float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
                                const int32_t* perm, int64_t a_rows) {
-  if (perm && (dtype != MOE_DTYPE_BF16 || !gelu || a_rows * K * 2 >= (int64_t)INT32_MAX))
-    return hipErrorInvalidValue;  // row gathering: first bf16 GEMM, A addressable with 31-bit offsets
+  if (perm && (dtype != MOE_DTYPE_BF16 || a_rows * K * 2 >= (int64_t)INT32_MAX))
+    return hipErrorInvalidValue;  // row gathering: bf16, A addressable with 31-bit offsets
   if (dtype == MOE_DTYPE_F32) {
     const int n_tiles = (int)ceil_div(N, F_BN);
     const int64_t m_tiles = (R + (int64_t)E * (F_BM - 1)) / F_BM;

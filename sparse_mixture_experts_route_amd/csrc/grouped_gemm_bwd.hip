@@ -1,0 +1,400 @@
+// Expert FFN GEMMs of the layer backward.
+//
+// The experts are independent FFNs ("Distributed training part 4", jesamkim's
+// AI tech blog, section 3); the MOSAIC summary ("Compute-Optimal Is Not
+// Cluster-Optimal", gist.science, method item 2) counts them as grouped GEMMs,
+// forward and backward. With U = X W1_e, H = GELU_tanh(U), Y = H W2_e per
+// expert row group, the backward needs
+//   dU  = (dYp W2_e^T) * GELU_tanh'(U)       rows grouped by expert (M-grouped)
+//   dX  = dU W1_e^T                           M-grouped
+//   dW2_e = H^T dYp,  dW1_e = X^T dU          K grouped: the expert's rows are
+//                                             the reduction dimension
+// so, next to the forward kernel's layout (A rows K-contiguous, B [K, N]
+// N-contiguous), operands appear transposed: the weights as [N, K]
+// (K-contiguous rows, e.g. W2_e [d_expert, d_model] for dYp W2_e^T) and the
+// activations as [K, M] (M-contiguous rows, e.g. H [rows, d_expert] for
+// H^T dYp).
+//
+// One kernel covers these cases with two operand stagings, both straight
+// from HBM to LDS (buffer_load_dwordx4 ... lds):
+//   * K-contiguous operand (a tile of 256 rows x 64 k): LDS [row][64] bf16,
+//     16-byte chunks XOR-swizzled by (row >> 1) & 7; fragments are
+//     ds_read_b128 (8 consecutive k of one row per lane);
+//   * MN-contiguous operand (64 k x 256 columns): LDS [k][256] bf16, chunks
+//     XOR-swizzled by 4 (k & 3); fragments are two ds_read_b64_tr_b16 (4
+//     consecutive k of one column per lane each).
+// Both give the v_mfma_f32_32x32x16_bf16 operand layout (lane l: row or
+// column l & 31, k 8 (l >> 5) .. + 7). Tiles are 256 x 256 with 8 waves (2 x 4
+// wave grid of 128 x 64), K steps of 64, two LDS stages (128 KB) and one
+// barrier per step; the next step's loads are issued right after the barrier
+// and the next sub-step's fragments are read while the current MFMAs run.
+//
+// M-grouped launches take their tiles from the expert row groups (offsets[],
+// as the forward kernel); K-grouped launches run E x (M / 256) x (N / 256)
+// tiles, each reducing over its expert's rows (zero rows: the tile stores
+// zeros), experts taken in order of decreasing row count so that the long
+// tiles of hot experts start first. The A operand of a K-grouped launch may
+// be gathered: row r read as row perm[r] of a [a_rows, M] matrix (dW1 reads
+// the tokens straight from x). The epilogue stages bf16 results through LDS
+// and writes whole row segments; EPI_DGELU multiplies by GELU_tanh'(U) at the
+// same positions before rounding.
+#include "common.h"
+#include "internal.h"
+#include "lds_dma.h"
+#include "tiles.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWM = 2, kWN = 4, kNW = kWM * kWN;
+constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;  // 128 x 64 per wave
+constexpr int kTM = kWTM / 32, kTN = kWTN / 32;     // MFMA tiles per wave
+constexpr int kKS = kBK / 16;                       // MFMA sub-steps per K step
+constexpr int kOp = 256 * kBK * 2;                  // bytes of one operand tile per stage (32 KB)
+constexpr int kStage = 2 * kOp;
+constexpr int kLd = kOp / 1024 / kNW;               // 1 KB loads per wave per operand per stage (4)
+constexpr int kThreads = kNW * kWave;
+
+enum { EPI_PLAIN = 0, EPI_DGELU = 1 };
+
+// GELU_tanh'(u) = (1 + tanh z)/2 + u/2 (1 - tanh^2 z) sqrt(2/pi) (1 + 3 * 0.044715 u^2),
+// z = sqrt(2/pi) (u + 0.044715 u^3); tanh z = 1 - 2 / (1 + e^(2z)) with the hardware exp2
+// and reciprocal (saturates to +-1 for large |z|).
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+  const float c = 0.7978845608028654f, a = 0.044715f;
+  const float z = c * fmaf(a * u, u * u, u);
+  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * z));
+  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * c * fmaf(3.0f * a, u * u, 1.0f);
+}
+
+struct BwdArgs {
+  const bf16_bits* A;   // M-grouped: [R, lda] rows; K-grouped: [rows, lda] (or [a_rows, lda] gathered)
+  const bf16_bits* B;   // M-grouped: expert e at B + e * b_estride, [N, ldb] rows (K-contiguous);
+                        // K-grouped: [rows, ldb] (N-contiguous)
+  bf16_bits* C;         // M-grouped: [R, N]; K-grouped: expert e at C + e * M * N, [M, N]
+  const bf16_bits* U;   // EPI_DGELU: [R, N], same positions as C
+  const int32_t* offsets;  // expert row groups (nullptr: one group of R rows)
+  const int32_t* perm;     // K-grouped gathered A: row r is row perm[r] of A
+  int64_t R, a_rows, b_estride;
+  int M, N, K, lda, ldb, E;
+};
+
+template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  __shared__ int s_tstart[257];
+  __shared__ int s_mtiles[256];
+  __shared__ int s_order[256];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm0 = (wave / kWN) * kWTM, wn0 = (wave % kWN) * kWTN;
+  lds_char* const lds = (lds_char*)smem;
+  const uint32_t lds_base = lds_addr(smem);
+  const int E = args.offsets ? args.E : 1;
+  const int n_tiles = (int)ceil_div(args.N, kBN);
+  const int m_fixed = (int)ceil_div(args.M, kBM);  // K-grouped: m tiles per expert
+
+  int total;
+  if constexpr (KGROUP) {
+    // experts by decreasing row count (ties: lower index first)
+    for (int e = tid; e < E; e += kThreads) {
+      const int c = args.offsets ? args.offsets[e + 1] - args.offsets[e] : (int)args.R;
+      int rank = 0;
+      for (int f = 0; f < E; ++f) {
+        const int cf = args.offsets ? args.offsets[f + 1] - args.offsets[f] : (int)args.R;
+        rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+      }
+      s_order[rank] = e;
+    }
+    __syncthreads();
+    total = E * m_fixed * n_tiles;
+  } else {
+    if (args.offsets) {
+      build_tile_list<kBM>(args.offsets, E, args.R, n_tiles, s_tstart, s_mtiles);
+    } else {
+      if (tid == 0) {
+        s_tstart[0] = 0;
+        s_mtiles[0] = (int)ceil_div(args.R, kBM);
+        s_tstart[1] = s_mtiles[0] * n_tiles;
+      }
+      __syncthreads();
+    }
+    total = s_tstart[E];
+  }
+
+  // ---- fragment read offsets (bytes within an operand tile of a stage)
+  // K-contiguous tile: row r at r * 128, chunk c at ((c ^ ((r >> 1) & 7)) << 4)
+  int kc_x[kKS];
+  {
+    const int sw = ((lane & 31) >> 1) & 7;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) kc_x[ks] = ((ks * 2 + (lane >> 5)) ^ sw) << 4;
+  }
+  // MN-contiguous tile: lane q of its 16-lane group reads k row (q >> 2) of a
+  // 4-row block, columns 4 (q & 3) .. + 3; lanes 32..63 take the upper 8 k
+  const int q = lane & 15, g = lane >> 4, kr = q >> 2;
+  auto mn_rd = [&](int col0) {
+    const int col = col0 + (g & 1) * 16 + (q & 3) * 4;
+    return ((g >> 1) * 8 + kr) * 512 + (((col >> 3) ^ (4 * kr)) << 4) + (col & 7) * 2;
+  };
+  int a_rd[kTM], b_rd[kTN];
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+    a_rd[mi] = A_MN ? mn_rd(wm0 + mi * 32) : (wm0 + mi * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+    b_rd[ni] = B_MN ? mn_rd(wn0 + ni * 32) : (wn0 + ni * 32 + (lane & 31)) * 128;
+
+  bf16x8 fa[2][kTM], fb[2][kTN];
+  auto read_frag = [&](const lds_char* op, bool mn, int rd, int ks) {
+    if (mn) {
+      const lds_char* p0 = op + ks * 16 * 512 + rd;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * 512));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    return *(const lds_bf16x8*)(op + rd + kc_x[ks]);
+  };
+  auto read_set = [&](int buf, int ks, int set) {
+    const lds_char* st = lds + buf * kStage;
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi) fa[set][mi] = read_frag(st, A_MN, a_rd[mi], ks);
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni) fb[set][ni] = read_frag(st + kOp, B_MN, b_rd[ni], ks);
+  };
+
+  // ---- DMA offsets of this lane (bytes), per operand kind
+  // K-contiguous tile: slot p holds row p / 8, chunk (p % 8) ^ ((row >> 1) & 7)
+  // MN-contiguous tile: slot p holds k row p / 32, chunk (p % 32) ^ (4 (k & 3))
+  int kc_row[kLd], kc_c8[kLd], mn_k[kLd], mn_c8[kLd];
+#pragma unroll
+  for (int i = 0; i < kLd; ++i) {
+    const int p = (wave * kLd + i) * kWave + lane;
+    kc_row[i] = p / 8;
+    kc_c8[i] = ((p % 8) ^ ((kc_row[i] >> 1) & 7)) * 8;
+    mn_k[i] = p / 32;
+    mn_c8[i] = ((p % 32) ^ (4 * (mn_k[i] & 3))) * 8;
+  }
+
+  f32x16 acc[kTM][kTN];
+
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    // ---- the tile: rows (M side), columns (N side), K range, operand bases
+    int e, mt, nt;
+    int64_t row0, row_end;  // M-grouped: rows of A and C; K-grouped: rows of the expert (K range)
+    if constexpr (KGROUP) {
+      const int per = m_fixed * n_tiles;
+      e = s_order[t / per];
+      const int local = t - (t / per) * per;
+      nt = local / m_fixed;
+      mt = local - nt * m_fixed;
+      row0 = args.offsets ? args.offsets[e] : 0;
+      row_end = args.offsets ? args.offsets[e + 1] : args.R;
+    } else {
+      int a0 = 0, a1 = E;
+      while (a1 - a0 > 1) {
+        const int mid = (a0 + a1) >> 1;
+        if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
+      }
+      e = a0;
+      const int local = t - s_tstart[e], mtl = s_mtiles[e];
+      nt = local / mtl;
+      mt = local - nt * mtl;
+      const int64_t g0 = args.offsets ? args.offsets[e] : 0;
+      row0 = g0 + (int64_t)mt * kBM;
+      row_end = args.offsets ? min((int64_t)args.offsets[e + 1], args.R) : args.R;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int m0 = KGROUP ? mt * kBM : 0, n0 = nt * kBN;
+    const int nk = KGROUP ? (int)ceil_div(row_end - row0, kBK) : args.K / kBK;
+
+    // operand descriptors (byte ranges end the valid data: loads past them read zero)
+    i32x4 rsA, rsB;
+    if constexpr (KGROUP) {
+      if constexpr (GATHER_A)
+        rsA = buffer_rsrc(args.A, (uint32_t)(args.a_rows * args.lda * 2));
+      else
+        rsA = buffer_rsrc(args.A + row0 * args.lda, (uint32_t)((row_end - row0) * args.lda * 2));
+      rsB = buffer_rsrc(args.B + row0 * args.ldb, (uint32_t)((row_end - row0) * args.ldb * 2));
+    } else {
+      rsA = buffer_rsrc(args.A + row0 * args.lda, (uint32_t)((row_end - row0) * args.lda * 2));
+      rsB = buffer_rsrc(args.B + (int64_t)e * args.b_estride, (uint32_t)((int64_t)args.N * args.ldb * 2));
+    }
+    // per-lane offsets that do not depend on the K step
+    uint32_t a_off[kLd], b_off[kLd];
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      if constexpr (A_MN)  // K-grouped: k row mn_k (+ 64 kt) of the group, columns m0 + c8
+        a_off[i] = (uint32_t)(mn_k[i] * args.lda + m0 + mn_c8[i]) * 2u;
+      else  // rows row0 + kc_row, k chunk c8 (+ 64 kt)
+        a_off[i] = (uint32_t)(kc_row[i] * args.lda + kc_c8[i]) * 2u;
+      if constexpr (B_MN)
+        b_off[i] = (uint32_t)(mn_k[i] * args.ldb + n0 + mn_c8[i]) * 2u;
+      else  // weight rows n0 + kc_row ([N, K] storage), columns past N point past the range
+        b_off[i] = n0 + kc_row[i] < args.N ? (uint32_t)((n0 + kc_row[i]) * args.ldb + kc_c8[i]) * 2u : 0xFFFFFFF0u;
+    }
+    // gathered A rows: the token of each k row of the next stage, looked up one stage ahead
+    int gat[kLd];
+    auto gather_rows = [&](int kt) {
+      if constexpr (GATHER_A) {
+#pragma unroll
+        for (int i = 0; i < kLd; ++i) {
+          const int64_t r = row0 + (int64_t)kt * kBK + mn_k[i];
+          gat[i] = r < row_end ? args.perm[r] : -1;
+        }
+      }
+    };
+    auto issue = [&](int kt, int buf) {
+      const uint32_t st = lds_base + buf * kStage;
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        const uint32_t la = st + (wave * kLd + i) * 1024;
+        if constexpr (GATHER_A) {
+          const uint32_t off = gat[i] >= 0 ? (uint32_t)(((int64_t)gat[i] * args.lda + m0 + mn_c8[i]) * 2) : 0xFFFFFFF0u;
+          buffer_load_lds16(rsA, off, 0u, la);
+        } else if constexpr (A_MN) {
+          buffer_load_lds16(rsA, a_off[i], (uint32_t)kt * kBK * args.lda * 2u, la);
+        } else {
+          buffer_load_lds16(rsA, a_off[i], (uint32_t)kt * kBK * 2u, la);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        const uint32_t lb = st + kOp + (wave * kLd + i) * 1024;
+        if constexpr (B_MN)
+          buffer_load_lds16(rsB, b_off[i], (uint32_t)kt * kBK * args.ldb * 2u, lb);
+        else
+          buffer_load_lds16(rsB, b_off[i], (uint32_t)kt * kBK * 2u, lb);
+      }
+    };
+
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+    if (nk > 0) {
+      gather_rows(0);
+      issue(0, 0);
+      if (nk > 1) gather_rows(1);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      wait_vmem<0>();
+      __syncthreads();  // stage kt is visible; every wave is done with buffer buf ^ 1
+      if (kt + 1 < nk) {
+        issue(kt + 1, buf ^ 1);
+        if (kt + 2 < nk) gather_rows(kt + 2);
+      }
+      read_set(buf, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const int set = ks & 1;
+        if (ks + 1 < kKS) read_set(buf, ks + 1, set ^ 1);
+#pragma unroll
+        for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < kTN; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with both buffers: the ring becomes the staging area
+
+    // ---- epilogue: lane holds row (lane & 31) of MFMA tile (mi, ni), columns
+    // 8 gq + 4 (lane >> 5) .. + 3; each wave stages its 128 x 64 piece as bf16
+    // (row-major, 16-byte chunks XOR-swizzled by the row) and writes row segments
+    constexpr int EP_ROW = kWTN * 2, EP_CH = kWTN / 8;
+    lds_char* const ep = lds + wave * (kWTM * EP_ROW);
+    const int64_t c_row0 = KGROUP ? m0 : row0;                       // first row of C of this tile
+    const int64_t c_rows = KGROUP ? (int64_t)args.M : row_end;       // rows of C (exclusive end)
+    bf16_bits* const Cb = args.C + (KGROUP ? (int64_t)e * args.M * args.N : 0);
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float v[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mi][ni][4 * gq + qq];
+          const int row = mi * 32 + (lane & 31);
+          if constexpr (EPI == EPI_DGELU) {
+            const int64_t grow = c_row0 + wm0 + row;
+            const int gcol = n0 + wn0 + ni * 32 + 8 * gq + 4 * (lane >> 5);
+            if (grow < c_rows && gcol < args.N) {
+              const u32x2 uu = *(const u32x2*)(args.U + grow * args.N + gcol);
+              v[0] *= gelu_tanh_grad(bf16_to_f32(uu[0] & 0xFFFFu));
+              v[1] *= gelu_tanh_grad(bf16_to_f32(uu[0] >> 16));
+              v[2] *= gelu_tanh_grad(bf16_to_f32(uu[1] & 0xFFFFu));
+              v[3] *= gelu_tanh_grad(bf16_to_f32(uu[1] >> 16));
+            }
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(v[0], v[1]);
+          o[1] = pack_bf16x2(v[2], v[3]);
+          const int ch = ni * 4 + gq;
+          *(__attribute__((address_space(3))) u32x2*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4) +
+                                                        (lane >> 5) * 8) = o;
+        }
+    // LDS operations of one wave complete in order: its own staged rows are readable now
+    const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Cb + c_row0 * args.N), (short)0, (int)max((int64_t)0, (c_rows - c_row0) * args.N * 2), kBufferFlags);
+    constexpr int ITERS = kWTM * EP_ROW / (16 * kWave);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int idx = it * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
+      const u32x4 v = *(__attribute__((address_space(3))) u32x4*)(ep + row * EP_ROW + ((ch ^ (row & (EP_CH - 1))) << 4));
+      const int n = n0 + wn0 + ch * 8;
+      const int off = n < args.N ? (int)(((int64_t)(wm0 + row) * args.N + n) * 2) : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
+    }
+    __syncthreads();  // the staging area is the next tile's ring
+  }
+}
+
+template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
+hipError_t launch(const BwdArgs& a, int64_t tiles, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  const int64_t grid = min(tiles, (int64_t)device_cus());
+  hipLaunchKernelGGL((gemm_bwd_kernel<KGROUP, A_MN, B_MN, GATHER_A, EPI>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gemm_nt(const bf16_bits* A, int lda, const int32_t* offsets, int64_t R, int E,
+                              const bf16_bits* B, int ldb, int64_t b_estride, bf16_bits* C, int N, int K,
+                              const bf16_bits* U, hipStream_t s) {
+  if (K % kBK != 0 || K <= 0 || N <= 0 || lda % 8 || ldb % 8 || N % 8) return hipErrorInvalidValue;
+  if (R * (int64_t)lda * 2 >= INT32_MAX || (int64_t)N * ldb * 2 >= INT32_MAX) return hipErrorInvalidValue;
+  BwdArgs a{};
+  a.A = A; a.B = B; a.C = C; a.U = U; a.offsets = offsets; a.perm = nullptr;
+  a.R = R; a.a_rows = R; a.b_estride = b_estride;
+  a.M = 0; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.E = E;
+  const int64_t tiles = (offsets ? (R + (int64_t)E * (kBM - 1)) / kBM : ceil_div(R, kBM)) * ceil_div(N, kBN);
+  if (U) return launch<false, false, false, false, EPI_DGELU>(a, tiles, s);
+  return launch<false, false, false, false, EPI_PLAIN>(a, tiles, s);
+}
+
+hipError_t launch_bwd_gemm_tn(const bf16_bits* A, int lda, const int32_t* perm, int64_t a_rows,
+                              const int32_t* offsets, int64_t R, int E, const bf16_bits* B, int ldb, bf16_bits* C,
+                              int M, int N, hipStream_t s) {
+  if (M <= 0 || N <= 0 || lda % 8 || ldb % 8 || M % 8 || N % 8) return hipErrorInvalidValue;
+  if ((perm ? a_rows : R) * (int64_t)lda * 2 >= INT32_MAX || R * (int64_t)ldb * 2 >= INT32_MAX)
+    return hipErrorInvalidValue;
+  BwdArgs a{};
+  a.A = A; a.B = B; a.C = C; a.U = nullptr; a.offsets = offsets; a.perm = perm;
+  a.R = R; a.a_rows = a_rows; a.b_estride = 0;
+  a.M = M; a.N = N; a.K = 0; a.lda = lda; a.ldb = ldb; a.E = E;
+  const int64_t tiles = (int64_t)(offsets ? E : 1) * ceil_div(M, kBM) * ceil_div(N, kBN);
+  if (perm) return launch<true, true, true, true, EPI_PLAIN>(a, tiles, s);
+  return launch<true, true, true, false, EPI_PLAIN>(a, tiles, s);
+}
+
+}  // namespace moe

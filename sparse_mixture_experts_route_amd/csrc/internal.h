@@ -52,8 +52,8 @@ hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* i
 // C[r] = act(A[r] B[e]) for rows r of every expert group e (offsets[E+1]).
 // A [R, K], B [E, K, N], C [R, N]; act = GELU_tanh or identity. `partials` is
 // workspace of grouped_gemm_partials_bytes() for split tiles (bf16 path).
-// With `perm` (bf16, gelu only) row r of A is row perm[r] of A [a_rows, K];
-// returns hipErrorInvalidValue when a_rows * K * 2 does not fit in 31 bits.
+// With `perm` (bf16) row r of A is row perm[r] of A [a_rows, K]; returns
+// hipErrorInvalidValue when a_rows * K * 2 does not fit in 31 bits.
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
                                float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
                                const int32_t* perm = nullptr, int64_t a_rows = 0);
@@ -63,5 +63,30 @@ size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv,
                           const float* gate, void* y, hipStream_t s);
+
+// ---- backward (bf16)
+// C[rows] = A[rows] B_e^T (* GELU_tanh'(U) when U is given) for the expert
+// row groups of offsets (nullptr: one group of R rows): A [R, lda] (K
+// contiguous), B_e = B + e * b_estride as [N, ldb] rows (K contiguous), C and
+// U [R, N]; K a multiple of 64.
+hipError_t launch_bwd_gemm_nt(const uint16_t* A, int lda, const int32_t* offsets, int64_t R, int E,
+                              const uint16_t* B, int ldb, int64_t b_estride, uint16_t* C, int N, int K,
+                              const uint16_t* U, hipStream_t s);
+// C_e = A_e^T B_e for every expert e (offsets; nullptr: one group of R rows),
+// reducing over the group's rows: A [rows, lda] (M contiguous; with perm,
+// row r is row perm[r] of A [a_rows, lda]), B [rows, ldb] (N contiguous),
+// C_e = C + e * M * N as [M, N]. Experts without rows get zeros.
+hipError_t launch_bwd_gemm_tn(const uint16_t* A, int lda, const int32_t* perm, int64_t a_rows,
+                              const int32_t* offsets, int64_t R, int E, const uint16_t* B, int ldb, uint16_t* C,
+                              int M, int N, hipStream_t s);
+hipError_t launch_bwd_combine(const moe_problem_t& p, const void* dy, const float* gate, const int32_t* idx,
+                              const int32_t* inv, const void* Y_perm, const float* logits, void* dYp,
+                              float* dlogit, uint16_t* dlogit_b, float* prob, int Ep, hipStream_t s);
+hipError_t launch_bwd_dx(const moe_problem_t& p, const void* dXp, const int32_t* inv, const void* dxr, void* dx,
+                         hipStream_t s);
+hipError_t launch_gelu_rows(const void* U, void* H, int64_t elems, hipStream_t s);
+int64_t bwd_stat_chunks(int64_t T);
+hipError_t launch_bwd_stats(const moe_problem_t& p, const float* prob, const float* dlogit, const int32_t* counts,
+                            float* part, float* load_frac, float* mean_prob, float* dbias, hipStream_t s);
 
 }  // namespace moe

@@ -102,6 +102,49 @@ ForwardWs carve_forward(Carver& c, const moe_problem_t& p) {
   return w;
 }
 
+// Training: what moe_forward_train keeps for moe_backward, then the backward's own buffers.
+struct TrainWs {
+  float *logits, *gate;                              // [T, E], [T, k]
+  int32_t *idx, *counts, *offsets, *perm, *inv;
+  void *U, *H, *y_perm;                              // [R, d_expert] x2, [R, d_model] (bf16)
+  PermuteWs pw;
+  float *route_part, *partials;
+  void *dYp, *dU, *dXp, *dxr;                        // [R, d], [R, de], [R, d], [T, d] (bf16)
+  float *dlogit, *prob, *stat_part;                  // [T, E], [T, E], [chunks, 2, E]
+  uint16_t* dlogit_b;                                // [T, E64] bf16, zero columns past E
+};
+
+inline int padded_experts(const moe_problem_t& p) { return (p.E + 63) / 64 * 64; }
+
+TrainWs carve_train(Carver& c, const moe_problem_t& p) {
+  const size_t R = (size_t)p.T * p.k, T = (size_t)p.T;
+  TrainWs w;
+  w.logits = c.take<float>(T * p.E);
+  w.gate = c.take<float>(R);
+  w.idx = c.take<int32_t>(R);
+  w.counts = c.take<int32_t>(p.E);
+  w.offsets = c.take<int32_t>(p.E + 1);
+  w.perm = c.take<int32_t>(R);
+  w.inv = c.take<int32_t>(R);
+  w.U = c.take<uint16_t>(R * p.d_expert);
+  w.H = c.take<uint16_t>(R * p.d_expert);
+  w.y_perm = c.take<uint16_t>(R * p.d_model);
+  w.pw = carve_permute(c, p);
+  w.route_part = carve_route(c, p);
+  const size_t pb = std::max(moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_model, p.d_expert, p.E),
+                             moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_expert, p.d_model, p.E));
+  w.partials = c.take<float>(pb / sizeof(float));
+  w.dYp = c.take<uint16_t>(R * p.d_model);
+  w.dU = c.take<uint16_t>(R * p.d_expert);
+  w.dXp = c.take<uint16_t>(R * p.d_model);
+  w.dxr = c.take<uint16_t>(T * p.d_model);
+  w.dlogit = c.take<float>(T * p.E);
+  w.prob = c.take<float>(T * p.E);
+  w.stat_part = c.take<float>((size_t)moe::bwd_stat_chunks(p.T) * 2 * p.E);
+  w.dlogit_b = c.take<uint16_t>(T * padded_experts(p));
+  return w;
+}
+
 size_t stage_bytes(const moe_problem_t& p, int32_t stage) {
   Carver c(nullptr);
   switch (stage) {
@@ -113,6 +156,9 @@ size_t stage_bytes(const moe_problem_t& p, int32_t stage) {
       break;
     case MOE_STAGE_ROUTE:
       carve_route(c, p);
+      break;
+    case MOE_STAGE_TRAIN:
+      carve_train(c, p);
       break;
     default:
       carve_forward(c, p);
@@ -138,7 +184,7 @@ MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, s
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
   if (stage != MOE_STAGE_PERMUTE && stage != MOE_STAGE_GROUPED_FFN && stage != MOE_STAGE_FORWARD &&
-      stage != MOE_STAGE_ROUTE)
+      stage != MOE_STAGE_ROUTE && stage != MOE_STAGE_TRAIN)
     return MOE_ERR_INVALID_ARGUMENT;
   *bytes = stage_bytes(*p, stage);
   return MOE_OK;
@@ -304,6 +350,91 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
     e = moe::launch_grouped_gemm(p->dtype, w.fw.h, w.offsets, W2, w.y_perm, w.fw.partials, R, p->d_expert,
                                  p->d_model, p->E, false, s);
   if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
+  return hip_status(e);
+}
+
+// Training path: bf16, x addressable by the gathering GEMMs, k <= 8, E a multiple of 8.
+inline bool train_supported(const moe_problem_t& p) {
+  return gather_supported(p) && p.k <= 8 && p.E % 8 == 0;
+}
+
+MOE_API moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void* w_router,
+                                       const float* router_bias, const void* W1, const void* W2, void* y, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !W1 || !W2 || !y || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(W1) || !aligned16(W2) || !aligned16(y) ||
+      !aligned16(ws) || (router_bias && !aligned16(router_bias)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!train_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_TRAIN)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const TrainWs w = carve_train(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = p->T * p->k;
+  hipError_t e = moe::launch_route(*p, x, w_router, router_bias, w.logits, w.idx, w.gate, w.route_part, s);
+  if (e == hipSuccess)
+    e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts,
+                                  w.pw.blockbase, s);
+  // U = x W1 per expert (rows read through perm), kept; H = GELU_tanh(U)
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.U, w.partials, R, p->d_model, p->d_expert, p->E,
+                                 false, s, w.perm, p->T);
+  if (e == hipSuccess) e = moe::launch_gelu_rows(w.U, w.H, R * p->d_expert, s);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, w.H, w.offsets, W2, w.y_perm, w.partials, R, p->d_expert, p->d_model,
+                                 p->E, false, s);
+  if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
+  return hip_status(e);
+}
+
+MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_router, const void* W1,
+                                  const void* W2, const void* dy, void* dx, void* dw_router, float* dbias,
+                                  void* dW1, void* dW2, float* load_frac, float* mean_prob, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !W1 || !W2 || !dy || !dx || !dw_router || !dW1 || !dW2 || !ws)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(W1) || !aligned16(W2) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(dw_router) || !aligned16(dW1) || !aligned16(dW2) || !aligned16(ws) ||
+      (dbias && !aligned16(dbias)) || (load_frac && !aligned16(load_frac)) || (mean_prob && !aligned16(mean_prob)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!train_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < stage_bytes(*p, MOE_STAGE_TRAIN)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Carver c(align_ws(ws));
+  const TrainWs w = carve_train(c, *p);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = p->T * p->k;
+  const int d = p->d_model, de = p->d_expert, Ep = padded_experts(*p);
+  typedef const uint16_t* cb;
+  hipError_t e = moe::launch_bwd_combine(*p, dy, w.gate, w.idx, w.inv, w.y_perm, w.logits, w.dYp, w.dlogit,
+                                         w.dlogit_b, w.prob, Ep, s);
+  // dU = (dYp W2_e^T) * GELU_tanh'(U), dX = dU W1_e^T
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_nt((cb)w.dYp, d, w.offsets, R, p->E, (cb)W2, d, (int64_t)de * d, (uint16_t*)w.dU, de,
+                                d, (cb)w.U, s);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_nt((cb)w.dU, de, w.offsets, R, p->E, (cb)W1, de, (int64_t)d * de, (uint16_t*)w.dXp, d,
+                                de, nullptr, s);
+  // dW2_e = H^T dYp, dW1_e = x[perm]^T dU over each expert's rows
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_tn((cb)w.H, de, nullptr, R, w.offsets, R, p->E, (cb)w.dYp, d, (uint16_t*)dW2, de, d,
+                                s);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_tn((cb)x, d, w.perm, p->T, w.offsets, R, p->E, (cb)w.dU, de, (uint16_t*)dW1, d, de,
+                                s);
+  // router: dx_r = dlogit W_r^T, dW_r = x^T dlogit (one group of T rows)
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_nt(w.dlogit_b, Ep, nullptr, p->T, 1, (cb)w_router, p->E, 0, (uint16_t*)w.dxr, d, Ep,
+                                nullptr, s);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gemm_tn((cb)x, d, nullptr, p->T, nullptr, p->T, 1, w.dlogit_b, Ep, (uint16_t*)dw_router, d,
+                                p->E, s);
+  if (e == hipSuccess) e = moe::launch_bwd_dx(*p, w.dXp, w.inv, w.dxr, dx, s);
+  if (e == hipSuccess && (dbias || load_frac || mean_prob))
+    e = moe::launch_bwd_stats(*p, w.prob, w.dlogit, w.counts, w.stat_part, load_frac, mean_prob, dbias, s);
   return hip_status(e);
 }
 

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "moe_workspace_size", "moe_route", "moe_route_ws", "moe_permute", "moe_permute_index", "moe_grouped_ffn",
-        "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_status_str"])
+        "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_forward_train", "moe_backward",
+        "moe_status_str"])
 
 
 def test_library_exports_every_declared_symbol(libmoe_path):
