@@ -113,6 +113,67 @@ def cpu_baseline(cfg, inp, sample_tokens):
                       f"{dt:.2f} s wall (NumPy float64, BLAS threads={threads}, host cpus={os.cpu_count()})"}
 
 
+def train_step(args, cfg, moe, inp, dev):
+    """A training step (forward keeping its activations, then the backward) on
+    one batch resident in HBM; HIP events around each half on the stream the
+    kernels run on. FLOPs: the six expert GEMMs (2 forward, 4 backward) of
+    2 T k d d_e each, plus the router's x W_r, dlogit W_r^T and x^T dlogit."""
+    import torch
+    from harness import make_dense
+    x, wr, b, W1, W2 = inp["x"], inp["w_router"], inp["router_bias"], inp["W1"], inp["W2"]
+    T, d, E, k, de = cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert
+    p = moe.make_problem(T, d, E, k, de, x.dtype)
+    ws = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_TRAIN), dtype=torch.uint8, device=dev)
+    bf = torch.bfloat16
+    y = torch.empty((T, d), dtype=bf, device=dev)
+    dy = make_dense((T, d), 1.0, seed=args.seed, tag=9, device=dev)
+    dx = torch.empty((T, d), dtype=bf, device=dev)
+    dwr = torch.empty((d, E), dtype=bf, device=dev)
+    db = torch.empty(E, dtype=torch.float32, device=dev)
+    dW1, dW2 = torch.empty_like(W1), torch.empty_like(W2)
+    lf = torch.empty(E, dtype=torch.float32, device=dev)
+    mp = torch.empty(E, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        moe.moe_forward_train(p, x, wr, b, W1, W2, y, ws)
+        if ev:
+            ev[1].record(stream)
+        moe.moe_backward(p, x, wr, W1, W2, dy, dx, dwr, db, dW1, dW2, lf, mp, ws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd = sorted(e[0].elapsed_time(e[1]) for e in evs)[args.steps // 2]
+    bwd = sorted(e[1].elapsed_time(e[2]) for e in evs)[args.steps // 2]
+    tot = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    R = T * k
+    gemm_flops = 12 * R * d * de
+    router_flops = 6 * T * d * E
+    tflops = (gemm_flops + router_flops) / (tot * 1e-3) / 1e12
+    bwd_tflops = (8 * R * d * de + 4 * T * d * E) / (bwd * 1e-3) / 1e12
+    return {
+        "metric": "MoE layer training step (forward keeping activations + backward) tokens/sec, 1 GPU",
+        "value": round(T / (tot * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(tot, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded normal inputs, dy and weights)",
+        "config": {**cfg.describe(), "parallelism": "none (1 GPU, all experts local)", "mode": "train"},
+        "forward_train_ms_median": round(fwd, 4), "backward_ms_median": round(bwd, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole training step: 6 expert GEMMs (12 T k d d_e flops) + router GEMMs"},
+        "backward_tflops": round(bwd_tflops, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +185,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=0,
                     help="batch size T instead of the workload's (e.g. 1..160 for decode-sized batches)")
     ap.add_argument("--k", type=int, default=0, help="experts per token instead of the workload's")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step instead: moe_forward_train + moe_backward (bf16)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -159,6 +222,10 @@ def main():
     x, wr, b, W1, W2 = inp["x"], inp["w_router"], inp["router_bias"], inp["W1"], inp["W2"]
     layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, x.dtype, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.train:
+        print(json.dumps(train_step(args, cfg, moe, inp, dev)), flush=True)
+        return
 
     # ---- per-phase region: the same work through the four stage entry points,
     # with HIP events between phases on the stream the kernels run on. It runs

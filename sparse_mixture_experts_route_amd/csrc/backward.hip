@@ -144,20 +144,34 @@ __global__ __launch_bounds__(256) void gelu_rows_kernel(const u32x4* __restrict_
 
 constexpr int kStatTokens = 256;  // tokens per partial sum
 
-// Per chunk of kStatTokens tokens (thread e owns expert e): sums of p[t, e] and dlogit[t, e]
+// Per chunk of kStatTokens tokens: sums of p[t, e] and dlogit[t, e]. With EP =
+// the next power of two >= E, thread (e = tid % EP, j = tid / EP) adds tokens
+// j, j + 256 / EP, ... of the chunk; the 256 / EP sums of an expert are then
+// added in j order (a fixed order: deterministic).
 __global__ __launch_bounds__(256) void bwd_stats_partial_kernel(const float* __restrict__ prob,
                                                                 const float* __restrict__ dlogit,
-                                                                float* __restrict__ part, int64_t T, int E) {
-  const int e = threadIdx.x;
-  if (e >= E) return;
+                                                                float* __restrict__ part, int64_t T, int E, int EP) {
+  __shared__ float s_p[256], s_d[256];
+  const int tid = threadIdx.x, e = tid % EP, j = tid / EP, tpe = 256 / EP;
   const int64_t t0 = (int64_t)blockIdx.x * kStatTokens, t1 = min(T, t0 + kStatTokens);
   float sp = 0.0f, sd = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) {
-    sp += prob[t * E + e];
-    sd += dlogit[t * E + e];
+  if (e < E)
+    for (int64_t t = t0 + j; t < t1; t += tpe) {
+      sp += prob[t * E + e];
+      sd += dlogit[t * E + e];
+    }
+  s_p[tid] = sp;
+  s_d[tid] = sd;
+  __syncthreads();
+  if (j == 0 && e < E) {
+    float ap = 0.0f, ad = 0.0f;
+    for (int jj = 0; jj < tpe; ++jj) {
+      ap += s_p[jj * EP + e];
+      ad += s_d[jj * EP + e];
+    }
+    part[((int64_t)blockIdx.x * 2) * E + e] = ap;
+    part[((int64_t)blockIdx.x * 2 + 1) * E + e] = ad;
   }
-  part[((int64_t)blockIdx.x * 2) * E + e] = sp;
-  part[((int64_t)blockIdx.x * 2 + 1) * E + e] = sd;
 }
 
 // Chunk sums added in chunk order (deterministic); outputs may be null
@@ -212,8 +226,10 @@ hipError_t launch_gelu_rows(const void* U, void* H, int64_t elems, hipStream_t s
 hipError_t launch_bwd_stats(const moe_problem_t& p, const float* prob, const float* dlogit, const int32_t* counts,
                             float* part, float* load_frac, float* mean_prob, float* dbias, hipStream_t s) {
   const int64_t chunks = bwd_stat_chunks(p.T);
+  int ep = 1;
+  while (ep < p.E) ep <<= 1;
   hipLaunchKernelGGL(bwd_stats_partial_kernel, dim3((unsigned)chunks), dim3(256), 0, s, prob, dlogit, part, p.T,
-                     p.E);
+                     p.E, ep);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_stats_final_kernel, dim3(1), dim3(256), 0, s, (const float*)part, chunks, counts, load_frac,

@@ -95,3 +95,77 @@ def test_backward_repeatable_and_workspace_reuse(moe):
     _, b = run_train(moe, cfg, inp, dy)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+def _sampled_weight_grads(x64, wr64, bias, W1, W2, dy64, k, dtype, route, samples):
+    """dW1_e[j, i] and dW2_e[i, j] for sampled (e, i, j), each as the sum over the
+    expert's rows that defines it: dW2_e[i, j] = sum_r H[r, i] dYp[r, j],
+    dW1_e[j, i] = sum_r x[token r, j] dU[r, i], with U[:, i] = X_e W1_e[:, i],
+    dU[r, i] = GELU'(U[r, i]) (dYp[r] . W2_e[i, :]) (float64, exact inputs)."""
+    gate = route["gate"]
+    out = []
+    for e, i, j in samples:
+        sel = np.argwhere(route["idx"] == e)          # (t, jsel), tokens in order
+        toks = sel[:, 0]
+        g = gate[sel[:, 0], sel[:, 1]]
+        w1 = oracle.decode(host_array(W1[e]), dtype)
+        w2 = oracle.decode(host_array(W2[e]), dtype)
+        X = x64[toks]
+        dYp = g[:, None] * dy64[toks]
+        u = X @ w1[:, i]
+        h = oracle.gelu_tanh(u)
+        du = oracle.gelu_tanh_grad(u) * (dYp @ w2[i, :])
+        out.append((float(h @ dYp[:, j]), float(X[:, j] @ du)))
+    return out
+
+
+FULL = ["mixtral_coarse", "fine_grained", "skewed", "large_sparse"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_backward_full_size_sampled(moe, name):
+    """The workloads at full size, as one training step runs them: dx on sampled
+    tokens (token-local: the oracle runs the backward of just those tokens),
+    sampled expert weight-gradient elements, and the load statistics."""
+    from harness import CONFIGS
+    cfg = CONFIGS[name]
+    announce(f"backward full {name}")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    dy = make_dense((cfg.T, cfg.d_model), 1.0, seed=0, tag=9, device="cuda")
+    _, g = run_train(moe, cfg, inp, dy)
+    x64 = oracle.decode(host_array(inp["x"]), "bf16")
+    wr64 = oracle.decode(host_array(inp["w_router"]), "bf16")
+    bias = host_array(inp["router_bias"])
+    dy64 = oracle.decode(host_array(dy), "bf16")
+    r = oracle.route(x64, wr64, bias, cfg.k)
+    counts = np.bincount(r["idx"].reshape(-1), minlength=cfg.E)
+    np.testing.assert_allclose(f64(g["load_frac"]), counts / (cfg.T * cfg.k), rtol=1e-6, atol=0)
+    np.testing.assert_allclose(f64(g["mean_prob"]), oracle.softmax_probs(r["logits"]).mean(axis=0), rtol=1e-4,
+                               atol=1e-7)
+    # dx of sampled tokens (no near-ties among them)
+    rng = np.random.default_rng(7)
+    cand = np.nonzero(~r["near_tie"])[0]
+    toks = np.sort(rng.choice(cand, 6, replace=False))
+    sub = oracle.backward64(x64[toks], wr64, lambda e: oracle.decode(host_array(inp["W1"][e]), "bf16"),
+                            lambda e: oracle.decode(host_array(inp["W2"][e]), "bf16"), cfg.k, dy64[toks],
+                            r["idx"][toks], r["logits"][toks])
+    err = rel_err(f64(g["dx"][torch.from_numpy(toks).cuda()]), sub["dx"])
+    print(f"{name}: dx rel err {err:.3e} on tokens {toks.tolist()}")
+    assert err <= TOL_BF16
+    # sampled weight-gradient elements of the busiest, a middle and the least used expert with rows
+    used = np.nonzero(counts > 0)[0]
+    order = used[np.argsort(-counts[used])]
+    experts = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    samples = [(e, int(rng.integers(cfg.d_expert)), int(rng.integers(cfg.d_model))) for e in experts for _ in range(4)]
+    if r["near_tie"].any():  # a near-tie token may be routed either way: its expert's sums may differ
+        tied = set(r["idx"][r["near_tie"]].reshape(-1).tolist())
+        samples = [s for s in samples if s[0] not in tied] or samples[:0]
+    ref = _sampled_weight_grads(x64, wr64, bias, inp["W1"], inp["W2"], dy64, cfg.k, "bf16", r, samples)
+    got2 = [float(g["dW2"][e, i, j]) for e, i, j in samples]
+    got1 = [float(g["dW1"][e, j, i]) for e, i, j in samples]
+    for name2, got, want in (("dW2", got2, [a for a, _ in ref]), ("dW1", got1, [b for _, b in ref])):
+        want = np.array(want)
+        scale = np.abs(want).max()
+        diff = np.abs(np.array(got) - want).max()
+        print(f"{name}: {name2} sampled max|d| {diff:.3e} of max|ref| {scale:.3e} over {len(want)} elements")
+        assert diff <= TOL_BF16 * scale
