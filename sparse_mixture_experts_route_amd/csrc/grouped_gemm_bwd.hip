@@ -38,6 +38,8 @@
 // the tokens straight from x). The epilogue stages bf16 results through LDS
 // and writes whole row segments; EPI_DGELU multiplies by GELU_tanh'(U) at the
 // same positions before rounding.
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 #include "lds_dma.h"
@@ -75,10 +77,13 @@ struct BwdArgs {
                         // K-grouped: [rows, ldb] (N-contiguous)
   bf16_bits* C;         // M-grouped: [R, N]; K-grouped: expert e at C + e * M * N, [M, N]
   const bf16_bits* U;   // EPI_DGELU: [R, N], same positions as C
-  const int32_t* offsets;  // expert row groups (nullptr: one group of R rows)
+  const int32_t* offsets;  // expert row groups (nullptr: one group of R rows, or, K-grouped,
+                           // E equal groups)
   const int32_t* perm;     // K-grouped gathered A: row r is row perm[r] of A
+  float* partials;         // M-grouped: float32 partial sums of split tiles (max_rem > 0)
   int64_t R, a_rows, b_estride;
   int M, N, K, lda, ldb, E;
+  int min_steps, max_rem;  // M-grouped split of the last round (split_leftover)
 };
 
 template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
@@ -93,7 +98,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   const int wm0 = (wave / kWN) * kWTM, wn0 = (wave % kWN) * kWTN;
   lds_char* const lds = (lds_char*)smem;
   const uint32_t lds_base = lds_addr(smem);
-  const int E = args.offsets ? args.E : 1;
+  const int E = (KGROUP || args.offsets) ? args.E : 1;
+  // K-grouped row group e: offsets[e] .. offsets[e + 1], or the e-th of E equal parts of R
+  auto grp = [&](int e) -> int64_t { return args.offsets ? (int64_t)args.offsets[e] : args.R * e / E; };
   const int n_tiles = (int)ceil_div(args.N, kBN);
   const int m_fixed = (int)ceil_div(args.M, kBM);  // K-grouped: m tiles per expert
 
@@ -101,10 +108,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   if constexpr (KGROUP) {
     // experts by decreasing row count (ties: lower index first)
     for (int e = tid; e < E; e += kThreads) {
-      const int c = args.offsets ? args.offsets[e + 1] - args.offsets[e] : (int)args.R;
+      const int64_t c = grp(e + 1) - grp(e);
       int rank = 0;
       for (int f = 0; f < E; ++f) {
-        const int cf = args.offsets ? args.offsets[f + 1] - args.offsets[f] : (int)args.R;
+        const int64_t cf = grp(f + 1) - grp(f);
         rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
       }
       s_order[rank] = e;
@@ -181,7 +188,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
 
   f32x16 acc[kTM][kTN];
 
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+  // ---- work items. K-grouped: tiles blockIdx.x, + gridDim.x, ... M-grouped:
+  // the tile list is cut into 8 contiguous ranges, one per XCD (blocks are dealt
+  // to the XCDs round robin), whole tiles round by round, then a small last
+  // round of long tiles split over the XCD's blocks by K steps (split_k); split
+  // shares write float32 partial sums that the fixup kernel adds in K order.
+  const int nkt = KGROUP ? 0 : args.K / kBK;
+  const int xcd = blockIdx.x % 8, nbk = gridDim.x / 8, jb = blockIdx.x / 8;
+  const int lo = KGROUP ? 0 : (int)((int64_t)total * xcd / 8);
+  SplitK sk{};
+  int n_items;
+  if constexpr (KGROUP) {
+    n_items = (int)blockIdx.x < total ? (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  } else {
+    const int hi = (int)((int64_t)total * (xcd + 1) / 8);
+    sk = split_k(hi - lo, nbk, jb, nkt, args.min_steps, args.max_rem);
+    n_items = sk.n_items;
+  }
+
+  for (int item = 0; item < n_items; ++item) {
+    int t, kb = 0, kn = nkt, slot = -1;
+    if constexpr (KGROUP) {
+      t = (int)blockIdx.x + item * (int)gridDim.x;
+    } else if (item < sk.full) {
+      t = lo + jb + item * nbk;
+    } else {
+      const int r = sk.r_first + (item - sk.full);
+      t = lo + sk.full * nbk + r;
+      const int64_t a0 = max(sk.s0, (int64_t)r * nkt), b0 = min(sk.s1, (int64_t)(r + 1) * nkt);
+      kb = (int)(a0 - (int64_t)r * nkt);
+      kn = (int)(b0 - a0);
+      slot = kn == nkt ? -1 : (int)blockIdx.x * 2 + (item - sk.full);
+    }
     // ---- the tile: rows (M side), columns (N side), K range, operand bases
     int e, mt, nt;
     int64_t row0, row_end;  // M-grouped: rows of A and C; K-grouped: rows of the expert (K range)
@@ -191,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       const int local = t - (t / per) * per;
       nt = local / m_fixed;
       mt = local - nt * m_fixed;
-      row0 = args.offsets ? args.offsets[e] : 0;
-      row_end = args.offsets ? args.offsets[e + 1] : args.R;
+      row0 = grp(e);
+      row_end = grp(e + 1);
     } else {
       int a0 = 0, a1 = E;
       while (a1 - a0 > 1) {
@@ -209,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
     }
     e = __builtin_amdgcn_readfirstlane(e);
     const int m0 = KGROUP ? mt * kBM : 0, n0 = nt * kBN;
-    const int nk = KGROUP ? (int)ceil_div(row_end - row0, kBK) : args.K / kBK;
+    const int nk = KGROUP ? (int)ceil_div(row_end - row0, kBK) : kn;
 
     // operand descriptors (byte ranges end the valid data: loads past them read zero)
     i32x4 rsA, rsB;
@@ -248,6 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       }
     };
     auto issue = [&](int kt, int buf) {
+      kt += kb;  // absolute K step (M-grouped split shares start at kb)
       const uint32_t st = lds_base + buf * kStage;
 #pragma unroll
       for (int i = 0; i < kLd; ++i) {
@@ -304,6 +343,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       }
     }
     __syncthreads();  // every wave is done with both buffers: the ring becomes the staging area
+    if (slot >= 0) {
+      // ---- a split share: float32 partial sums in the accumulator layout
+      // (thread-major per MFMA register group, 16 bytes per lane), the layout
+      // of the forward kernel's 8-wave 256 x 256 tile that the fixup reads
+      float* const dst = args.partials + (int64_t)slot * (kBM * kBN);
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            f32x4 v;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mi][ni][4 * gq + qq];
+            *(f32x4*)(dst + ((int64_t)((mi * kTN + ni) * 4 + gq) * (kNW * kWave) + tid) * 4) = v;
+          }
+      continue;  // block-uniform: every thread takes this branch together
+    }
 
     // ---- epilogue: lane holds row (lane & 31) of MFMA tile (mi, ni), columns
     // 8 gq + 4 (lane >> 5) .. + 3; each wave stages its 128 x 64 piece as bf16
@@ -357,29 +414,86 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   }
 }
 
+// persistent grid: one block per CU at most, a multiple of 8 (the XCD ranges);
+// MOE_GEMM_MAX_BLOCKS=<n> lowers the cap as for the forward GEMMs (several
+// rounds on small problems: exercises the split of the last round)
+int64_t bwd_grid(int64_t tiles) {
+  int64_t slots = (int64_t)device_cus() / 8 * 8;
+  const char* cap = getenv("MOE_GEMM_MAX_BLOCKS");
+  if (cap && cap[0]) slots = min(slots, max((int64_t)8, (int64_t)atoi(cap) / 8 * 8));
+  return max((int64_t)8, min(ceil_div(tiles, 8) * 8, slots));
+}
+
+int64_t nt_tiles_ub(int64_t R, int E, int N, bool grouped) {
+  return (grouped ? (R + (int64_t)E * (kBM - 1)) / kBM : ceil_div(R, kBM)) * ceil_div(N, kBN);
+}
+
 template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
-hipError_t launch(const BwdArgs& a, int64_t tiles, hipStream_t s) {
-  if (tiles <= 0) return hipSuccess;
-  const int64_t grid = min(tiles, (int64_t)device_cus());
+hipError_t launch(const BwdArgs& a, int64_t grid, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bwd_kernel<KGROUP, A_MN, B_MN, GATHER_A, EPI>), dim3((unsigned)grid), dim3(kThreads), 0,
                      s, a);
   return hipGetLastError();
 }
 
+constexpr int kStatRowsPerSplit = 256;  // at least four K steps per split of x^T dlogit
+
+__global__ __launch_bounds__(256) void sum_splits_kernel(const u32x4* __restrict__ part, int splits, int64_t n_vecs,
+                                                         u32x4* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_vecs; i += (int64_t)gridDim.x * 256) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sp = 0; sp < splits; ++sp) {
+      const u32x4 v = part[(int64_t)sp * n_vecs + i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(v[q] & 0xFFFFu);
+        acc[2 * q + 1] += bf16_to_f32(v[q] >> 16);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    out[i] = o;
+  }
+}
+
 }  // namespace
+
+size_t bwd_partials_bytes(int64_t R, int E, int N) {
+  return (size_t)bwd_grid(nt_tiles_ub(R, E, N, true)) * 2 * kBM * kBN * sizeof(float);
+}
+
+int bwd_router_splits(int64_t T, int d, int E) {
+  const int64_t per = ceil_div(d, kBM) * ceil_div(E, kBN);  // tiles of one split
+  int64_t s = min((int64_t)device_cus() / per, T / kStatRowsPerSplit);
+  return (int)max((int64_t)1, min(s, (int64_t)32));
+}
+
+hipError_t launch_sum_splits(const bf16_bits* part, int splits, int64_t n, bf16_bits* out, hipStream_t s) {
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n_vecs = n / 8;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)max((int64_t)1, min(ceil_div(n_vecs, 256), (int64_t)1024))),
+                     dim3(256), 0, s, (const u32x4*)part, splits, n_vecs, (u32x4*)out);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_gemm_nt(const bf16_bits* A, int lda, const int32_t* offsets, int64_t R, int E,
                               const bf16_bits* B, int ldb, int64_t b_estride, bf16_bits* C, int N, int K,
-                              const bf16_bits* U, hipStream_t s) {
+                              const bf16_bits* U, float* partials, hipStream_t s) {
   if (K % kBK != 0 || K <= 0 || N <= 0 || lda % 8 || ldb % 8 || N % 8) return hipErrorInvalidValue;
   if (R * (int64_t)lda * 2 >= INT32_MAX || (int64_t)N * ldb * 2 >= INT32_MAX) return hipErrorInvalidValue;
   BwdArgs a{};
-  a.A = A; a.B = B; a.C = C; a.U = U; a.offsets = offsets; a.perm = nullptr;
+  a.A = A; a.B = B; a.C = C; a.U = U; a.offsets = offsets; a.perm = nullptr; a.partials = partials;
   a.R = R; a.a_rows = R; a.b_estride = b_estride;
   a.M = 0; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.E = E;
-  const int64_t tiles = (offsets ? (R + (int64_t)E * (kBM - 1)) / kBM : ceil_div(R, kBM)) * ceil_div(N, kBN);
-  if (U) return launch<false, false, false, false, EPI_DGELU>(a, tiles, s);
-  return launch<false, false, false, false, EPI_PLAIN>(a, tiles, s);
+  const int64_t grid = bwd_grid(nt_tiles_ub(R, E, N, offsets != nullptr));
+  const int nb = (int)(grid / 8);
+  a.min_steps = split_min_steps();
+  // the split needs the fixup's tile enumeration (expert groups) and a plain epilogue
+  a.max_rem = (partials && offsets && !U) ? nb / 3 : 0;
+  hipError_t e = U ? launch<false, false, false, false, EPI_DGELU>(a, grid, s)
+                   : launch<false, false, false, false, EPI_PLAIN>(a, grid, s);
+  if (e != hipSuccess || a.max_rem == 0) return e;
+  return launch_split_fixup_256(offsets, partials, C, R, K / kBK, N, E, nb, a.min_steps, a.max_rem, s);
 }
 
 hipError_t launch_bwd_gemm_tn(const bf16_bits* A, int lda, const int32_t* perm, int64_t a_rows,
@@ -389,12 +503,15 @@ hipError_t launch_bwd_gemm_tn(const bf16_bits* A, int lda, const int32_t* perm, 
   if ((perm ? a_rows : R) * (int64_t)lda * 2 >= INT32_MAX || R * (int64_t)ldb * 2 >= INT32_MAX)
     return hipErrorInvalidValue;
   BwdArgs a{};
-  a.A = A; a.B = B; a.C = C; a.U = nullptr; a.offsets = offsets; a.perm = perm;
+  a.A = A; a.B = B; a.C = C; a.U = nullptr; a.offsets = offsets; a.perm = perm; a.partials = nullptr;
   a.R = R; a.a_rows = a_rows; a.b_estride = 0;
   a.M = M; a.N = N; a.K = 0; a.lda = lda; a.ldb = ldb; a.E = E;
-  const int64_t tiles = (int64_t)(offsets ? E : 1) * ceil_div(M, kBM) * ceil_div(N, kBN);
-  if (perm) return launch<true, true, true, true, EPI_PLAIN>(a, tiles, s);
-  return launch<true, true, true, false, EPI_PLAIN>(a, tiles, s);
+  a.min_steps = 0; a.max_rem = 0;
+  const int64_t tiles = (int64_t)E * ceil_div(M, kBM) * ceil_div(N, kBN);
+  const int64_t grid = min(tiles, (int64_t)device_cus());
+  if (tiles <= 0) return hipSuccess;
+  if (perm) return launch<true, true, true, true, EPI_PLAIN>(a, grid, s);
+  return launch<true, true, true, false, EPI_PLAIN>(a, grid, s);
 }
 
 }  // namespace moe

@@ -71,14 +71,26 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int3
 // U [R, N]; K a multiple of 64.
 hipError_t launch_bwd_gemm_nt(const uint16_t* A, int lda, const int32_t* offsets, int64_t R, int E,
                               const uint16_t* B, int ldb, int64_t b_estride, uint16_t* C, int N, int K,
-                              const uint16_t* U, hipStream_t s);
-// C_e = A_e^T B_e for every expert e (offsets; nullptr: one group of R rows),
+                              const uint16_t* U, float* partials, hipStream_t s);
+// With `partials` (bwd_partials_bytes) and no U, a small last round of long
+// tiles is split over the blocks by K steps and completed by the fixup.
+// C_e = A_e^T B_e for every expert e (offsets; nullptr: E equal groups of R rows),
 // reducing over the group's rows: A [rows, lda] (M contiguous; with perm,
 // row r is row perm[r] of A [a_rows, lda]), B [rows, ldb] (N contiguous),
 // C_e = C + e * M * N as [M, N]. Experts without rows get zeros.
 hipError_t launch_bwd_gemm_tn(const uint16_t* A, int lda, const int32_t* perm, int64_t a_rows,
                               const int32_t* offsets, int64_t R, int E, const uint16_t* B, int ldb, uint16_t* C,
                               int M, int N, hipStream_t s);
+// Split-tile fixup of an 8-wave 256 x 256 row-grouped launch (no activation),
+// and the split threshold in K steps (MOE_GEMM_SPLIT_MIN_STEPS overrides it).
+hipError_t launch_split_fixup_256(const int32_t* offsets, const float* partials, uint16_t* C, int64_t R, int nk, int N,
+                                  int E, int nb, int min_steps, int max_rem, hipStream_t s);
+int split_min_steps();
+// Float32 partial-sum bytes launch_bwd_gemm_nt may use for R rows, E groups, N columns.
+size_t bwd_partials_bytes(int64_t R, int E, int N);
+// Rows of x^T dlogit per split of the router weight gradient, and the number of splits.
+int bwd_router_splits(int64_t T, int d, int E);
+hipError_t launch_sum_splits(const uint16_t* part, int splits, int64_t n, uint16_t* out, hipStream_t s);
 hipError_t launch_bwd_combine(const moe_problem_t& p, const void* dy, const float* gate, const int32_t* idx,
                               const int32_t* inv, const void* Y_perm, const float* logits, void* dYp,
                               float* dlogit, uint16_t* dlogit_b, float* prob, int Ep, hipStream_t s);

@@ -109,6 +109,7 @@ struct TrainWs {
   void *U, *H, *y_perm;                              // [R, d_expert] x2, [R, d_model] (bf16)
   PermuteWs pw;
   float *route_part, *partials;
+  uint16_t* dwr_part;                                // [splits, d, E] bf16: x^T dlogit per token split
   void *dYp, *dU, *dXp, *dxr;                        // [R, d], [R, de], [R, d], [T, d] (bf16)
   float *dlogit, *prob, *stat_part;                  // [T, E], [T, E], [chunks, 2, E]
   uint16_t* dlogit_b;                                // [T, E64] bf16, zero columns past E
@@ -131,9 +132,11 @@ TrainWs carve_train(Carver& c, const moe_problem_t& p) {
   w.y_perm = c.take<uint16_t>(R * p.d_model);
   w.pw = carve_permute(c, p);
   w.route_part = carve_route(c, p);
-  const size_t pb = std::max(moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_model, p.d_expert, p.E),
-                             moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_expert, p.d_model, p.E));
+  const size_t pb = std::max({moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_model, p.d_expert, p.E),
+                              moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_expert, p.d_model, p.E),
+                              moe::bwd_partials_bytes((int64_t)R, p.E, p.d_model)});
   w.partials = c.take<float>(pb / sizeof(float));
+  w.dwr_part = c.take<uint16_t>((size_t)moe::bwd_router_splits(p.T, p.d_model, p.E) * p.d_model * p.E);
   w.dYp = c.take<uint16_t>(R * p.d_model);
   w.dU = c.take<uint16_t>(R * p.d_expert);
   w.dXp = c.take<uint16_t>(R * p.d_model);
@@ -414,10 +417,10 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   // dU = (dYp W2_e^T) * GELU_tanh'(U), dX = dU W1_e^T
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_nt((cb)w.dYp, d, w.offsets, R, p->E, (cb)W2, d, (int64_t)de * d, (uint16_t*)w.dU, de,
-                                d, (cb)w.U, s);
+                                d, (cb)w.U, nullptr, s);
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_nt((cb)w.dU, de, w.offsets, R, p->E, (cb)W1, de, (int64_t)d * de, (uint16_t*)w.dXp, d,
-                                de, nullptr, s);
+                                de, nullptr, w.partials, s);
   // dW2_e = H^T dYp, dW1_e = x[perm]^T dU over each expert's rows
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_tn((cb)w.H, de, nullptr, R, w.offsets, R, p->E, (cb)w.dYp, d, (uint16_t*)dW2, de, d,
@@ -428,10 +431,15 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   // router: dx_r = dlogit W_r^T, dW_r = x^T dlogit (one group of T rows)
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_nt(w.dlogit_b, Ep, nullptr, p->T, 1, (cb)w_router, p->E, 0, (uint16_t*)w.dxr, d, Ep,
-                                nullptr, s);
+                                nullptr, nullptr, s);
+  // x^T dlogit over `splits` equal token ranges (one tile row each would leave
+  // most CUs idle), then the bf16 partial products added in split order
+  const int splits = moe::bwd_router_splits(p->T, d, p->E);
   if (e == hipSuccess)
-    e = moe::launch_bwd_gemm_tn((cb)x, d, nullptr, p->T, nullptr, p->T, 1, w.dlogit_b, Ep, (uint16_t*)dw_router, d,
-                                p->E, s);
+    e = moe::launch_bwd_gemm_tn((cb)x, d, nullptr, p->T, nullptr, p->T, splits, w.dlogit_b, Ep,
+                                splits > 1 ? w.dwr_part : (uint16_t*)dw_router, d, p->E, s);
+  if (e == hipSuccess && splits > 1)
+    e = moe::launch_sum_splits(w.dwr_part, splits, (int64_t)d * p->E, (uint16_t*)dw_router, s);
   if (e == hipSuccess) e = moe::launch_bwd_dx(*p, w.dXp, w.inv, w.dxr, dx, s);
   if (e == hipSuccess && (dbias || load_frac || mean_prob))
     e = moe::launch_bwd_stats(*p, w.prob, w.dlogit, w.counts, w.stat_part, load_frac, mean_prob, dbias, s);

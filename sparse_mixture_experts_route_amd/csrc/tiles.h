@@ -1,5 +1,5 @@
-// Tile list of the grouped GEMMs over ragged expert row groups, shared by the
-// forward and backward kernels.
+// Tile list of the grouped GEMMs over ragged expert row groups and the split
+// of a persistent launch's last round, shared by the forward and backward kernels.
 #pragma once
 
 #include "common.h"
@@ -44,6 +44,57 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
     if (lane == kWave - 1) tstart[E] = incl;
   }
   __syncthreads();
+}
+
+// Work of one block of a persistent launch over `tiles` tiles of `nk` K steps
+// shared by `nb` blocks (index j): `full` whole tiles (tiles j, j + nb, ...),
+// then units [s0, s1) of the remaining rem * nk (tile, K step) units, counted
+// tile-major over the last `rem` tiles; they touch leftover tiles
+// r_first .. r_first + n_items - full - 1 (at most two, as rem < nb).
+// The leftover tiles are split only when they fill at most a third of a round
+// (a fuller last round runs on partly idle CUs anyway) and when the K steps it
+// saves, (nb - rem) / nb of a tile, outweigh the partial-sum traffic and the
+// fixup launch, which cost about as much as `min_steps` K steps (24 measured
+// on gfx950 with 256 x 256 tiles).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+struct SplitK {
+  int full, rem, r_first, n_items;
+  int64_t s0, s1;
+};
+
+constexpr int kSplitMinSteps = 24;
+
+// `max_rem` caps the leftover tiles that may be split: nb / 3 for the tiles
+// that fill the matrix cores, nb - 1 for the small-M tile of decode-sized
+// batches, whose one partly filled round would otherwise leave most blocks
+// idle while a few stream whole weight slabs.
+__host__ __device__ __forceinline__ bool split_leftover(int rem, int nb, int nk, int min_steps, int max_rem) {
+  return rem > 0 && rem <= max_rem && (int64_t)nk * (nb - rem) >= (int64_t)min_steps * nb;
+}
+
+__device__ __forceinline__ SplitK split_k(int tiles, int nb, int j, int nk, int min_steps, int max_rem) {
+  SplitK r;
+  r.full = tiles / nb;
+  r.rem = tiles - r.full * nb;
+  if (!split_leftover(r.rem, nb, nk, min_steps, max_rem)) {
+    r.full += j < r.rem ? 1 : 0;  // one more round of whole tiles for the first rem blocks
+    r.rem = 0;
+    r.s0 = r.s1 = 0;
+    r.r_first = 0;
+    r.n_items = r.full;
+    return r;
+  }
+  const int64_t W = (int64_t)r.rem * nk;
+  r.s0 = W * j / nb;
+  r.s1 = W * (j + 1) / nb;
+  r.r_first = r.s1 > r.s0 ? (int)(r.s0 / nk) : 0;
+  const int n_rem = r.s1 > r.s0 ? (int)((r.s1 - 1) / nk) - r.r_first + 1 : 0;
+  r.n_items = r.full + n_rem;
+  return r;
 }
 
 }  // namespace moe

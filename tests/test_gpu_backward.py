@@ -84,6 +84,34 @@ def test_backward_against_oracle(moe, name, over):
         assert torch.count_nonzero(g["dW1"][e]) == 0 and torch.count_nonzero(g["dW2"][e]) == 0
 
 
+@pytest.mark.parametrize("blocks", [24, 64])
+def test_backward_split_last_round(moe, blocks):
+    """A capped persistent grid gives the row-grouped backward GEMMs several
+    rounds of tiles and a small last round split over the blocks by K steps
+    (float32 partial sums added by the fixup), and x^T dlogit split over
+    token ranges: the gradients are those of the unsplit run."""
+    import os
+    cfg = scaled_config("skewed", T=1200, d_model=512, E=16, k=4, d_expert=256, suffix="bwd")
+    announce(f"backward split blocks={blocks}")
+    inp = make_inputs(cfg, seed=6, device="cuda")
+    dy = make_dense((cfg.T, cfg.d_model), 1.0, seed=6, tag=9, device="cuda")
+    env = {"MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_SPLIT_MIN_STEPS": "0"}
+    os.environ.update(env)
+    try:
+        _, g = run_train(moe, cfg, inp, dy)
+    finally:
+        for key in env:
+            del os.environ[key]
+    h = {kk: host_array(v) for kk, v in inp.items()}
+    ref = oracle.backward(h["x"], h["w_router"], h["router_bias"], h["W1"], h["W2"], cfg.k, cfg.dtype,
+                          host_array(dy))
+    assert not ref["near_tie"].any()
+    for key in ("dx", "dw_router", "dW1", "dW2"):
+        err = rel_err(f64(g[key]), ref[key])
+        print(f"split blocks={blocks} {key}: rel err {err:.3e}")
+        assert err <= TOL_BF16, key
+
+
 def test_backward_repeatable_and_workspace_reuse(moe):
     """Two backward calls on one training workspace give identical results (no
     atomics, fixed summation orders), and a second training step reuses it."""
