@@ -322,26 +322,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       issue(0, 0);
       if (nk > 1) gather_rows(1);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      wait_vmem<0>();
-      __syncthreads();  // stage kt is visible; every wave is done with buffer buf ^ 1
-      if (kt + 1 < nk) {
-        issue(kt + 1, buf ^ 1);
-        if (kt + 2 < nk) gather_rows(kt + 2);
+    // a wave whose rows all lie past its group's end (the last, partly filled
+    // M tile of a row-grouped launch) skips its fragment reads and MFMAs but
+    // still issues its share of the loads and joins the barriers
+    auto kloop = [&](auto live_c) {
+      constexpr bool LIVE = decltype(live_c)::value;
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        wait_vmem<0>();
+        __syncthreads();  // stage kt is visible; every wave is done with buffer buf ^ 1
+        if (kt + 1 < nk) {
+          issue(kt + 1, buf ^ 1);
+          if (kt + 2 < nk) gather_rows(kt + 2);
+        }
+        if constexpr (LIVE) {
+          read_set(buf, 0, 0);
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks) {
+            const int set = ks & 1;
+            if (ks + 1 < kKS) read_set(buf, ks + 1, set ^ 1);
+#pragma unroll
+            for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+              for (int ni = 0; ni < kTN; ++ni)
+                acc[mi][ni] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
+          }
+        }
       }
-      read_set(buf, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const int set = ks & 1;
-        if (ks + 1 < kKS) read_set(buf, ks + 1, set ^ 1);
-#pragma unroll
-        for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < kTN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
-      }
-    }
+    };
+    if (KGROUP || row_end - row0 > wm0)
+      kloop(BoolC<true>{});
+    else
+      kloop(BoolC<false>{});
     __syncthreads();  // every wave is done with both buffers: the ring becomes the staging area
     if (slot >= 0) {
       // ---- a split share: float32 partial sums in the accumulator layout
