@@ -53,7 +53,7 @@ def gemm_source_hash():
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("grouped_gemm.hip", "common.h"):
+    for f in ("grouped_gemm.hip", "tiles.h", "common.h"):
         text = open(os.path.join(ROOT, "sparse_mixture_experts_route_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
