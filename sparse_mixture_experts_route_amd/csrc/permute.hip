@@ -10,7 +10,8 @@
 //           selected expert e (LDS atomicOr: the result does not depend on
 //           the order of the atomics); counts per (block, expert) = popcounts.
 //   scan    one workgroup: counts[e] over blocks, offsets[] as the exclusive
-//           prefix sum over experts, and the first row of every (block, expert).
+//           prefix sum over experts, and the first row of every (block, expert),
+//           from the per-block counts staged in LDS.
 //   scatter the row of selection (t, j) is the base of (block, e) plus the
 //           number of tokens before t in the block that selected e (popcount
 //           of the mask below t), so rows follow token order inside a group.
@@ -61,34 +62,91 @@ __global__ __launch_bounds__(kTB) void hist_kernel(const int32_t* __restrict__ i
   }
 }
 
-// One workgroup of 256 threads, thread e owns expert e.
-__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blockcounts, int64_t nb, int E,
-                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ blockbase) {
-  __shared__ int32_t s[256];
-  const int e = threadIdx.x;
-  int32_t total = 0;
-  if (e < E)
-    for (int64_t b = 0; b < nb; ++b) total += blockcounts[b * E + e];
-  s[e] = total;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the 256 slots
-  for (int o = 1; o < 256; o <<= 1) {
-    const int32_t v = e >= o ? s[e - o] : 0;
+// One workgroup. The per-block counts come into LDS with coalesced loads, in
+// chunks of whole blocks when they do not fit at once. Thread (q, e) owns
+// expert e and a contiguous quarter of the chunk's blocks. The first pass
+// gives the totals per expert, then their exclusive prefix sum over experts
+// is the offsets. The second pass writes the first row of every
+// (block, expert): offsets[e] plus the counts of e in the earlier blocks.
+constexpr int kScanThreads = 1024;
+constexpr int kScanQ = kScanThreads / 256;  // threads per expert
+constexpr int kScanLds = 16384;             // int32 counts staged per chunk
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blockcounts, int64_t nb,
+                                                            int E, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ blockbase) {
+  __shared__ int32_t s_c[kScanLds];
+  __shared__ int32_t s_part[kScanQ][256];
+  __shared__ int32_t s_run[256];
+  const int tid = threadIdx.x, e = tid % 256, q = tid / 256;
+  const int64_t cb = kScanLds / E;  // blocks per chunk (E <= 256, so at least 64)
+  const int64_t nchunks = (nb + cb - 1) / cb;
+  auto load_chunk = [&](int64_t b0, int64_t nbc) {
+    const int32_t* src = blockcounts + b0 * E;
+    for (int64_t i = tid; i < nbc * E; i += kScanThreads) s_c[i] = src[i];
+  };
+  // pass 1: totals per expert
+  int32_t part = 0;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t b0 = c * cb, nbc = min(cb, nb - b0);
+    __syncthreads();  // the previous chunk has been read
+    load_chunk(b0, nbc);
     __syncthreads();
-    s[e] += v;
+    if (e < E)
+      for (int64_t b = nbc * q / kScanQ; b < nbc * (q + 1) / kScanQ; ++b) part += s_c[b * E + e];
+  }
+  s_part[q][e] = part;
+  __syncthreads();
+  int32_t total = 0;
+  if (q == 0) {
+#pragma unroll
+    for (int i = 0; i < kScanQ; ++i) total += s_part[i][e];
+    s_run[e] = total;
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 256 expert slots (slots >= E hold 0)
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t v = (q == 0 && e >= o) ? s_run[e - o] : 0;
+    __syncthreads();
+    if (q == 0) s_run[e] += v;
     __syncthreads();
   }
-  const int32_t excl = s[e] - total;
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = excl;
-    if (e == E - 1) offsets[E] = s[e];
-    int32_t run = excl;
-    for (int64_t b = 0; b < nb; ++b) {
-      const int32_t c = blockcounts[b * E + e];
-      blockbase[b * E + e] = run;
-      run += c;
+  if (q == 0) {
+    const int32_t incl = s_run[e];
+    if (e < E) {
+      counts[e] = total;
+      offsets[e] = incl - total;
+      if (e == E - 1) offsets[E] = incl;
+    }
+    s_run[e] = incl - total;  // running first row of expert e, from offsets[e]
+  }
+  // pass 2: first row of every (block, expert)
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t b0 = c * cb, nbc = min(cb, nb - b0);
+    if (nchunks > 1) {
+      __syncthreads();
+      load_chunk(b0, nbc);
+    }
+    __syncthreads();
+    const int64_t lo = nbc * q / kScanQ, hi = nbc * (q + 1) / kScanQ;
+    int32_t sum = 0;
+    if (e < E)
+      for (int64_t b = lo; b < hi; ++b) sum += s_c[b * E + e];
+    s_part[q][e] = sum;
+    __syncthreads();
+    if (e < E) {
+      int32_t run = s_run[e];
+      for (int i = 0; i < q; ++i) run += s_part[i][e];
+      for (int64_t b = lo; b < hi; ++b) {
+        blockbase[(b0 + b) * E + e] = run;
+        run += s_c[b * E + e];
+      }
+    }
+    __syncthreads();
+    if (q == 0) {
+#pragma unroll
+      for (int i = 0; i < kScanQ; ++i) s_run[e] += s_part[i][e];
     }
   }
 }
@@ -97,22 +155,34 @@ __global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ blockbase,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ uint32_t mask[256][kWords];
+  __shared__ int32_t s_base[256];
   const int64_t t0 = (int64_t)blockIdx.x * kTB;
+  // this block's first row per expert (visible after build_mask's barriers)
+  if ((int)threadIdx.x < E) s_base[threadIdx.x] = blockbase[(int64_t)blockIdx.x * E + threadIdx.x];
   build_mask(idx, T, k, E, mask, t0);
   const int64_t t = t0 + threadIdx.x;
   if (t >= T) return;
   const int w = threadIdx.x >> 5;
   const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    int32_t r = -1;
-    if ((unsigned)e < (unsigned)E) {
-      int rank = __popc(mask[e][w] & below);
-      for (int w2 = 0; w2 < w; ++w2) rank += __popc(mask[e][w2]);
-      r = blockbase[(int64_t)blockIdx.x * E + e] + rank;
-      perm[r] = (int32_t)t;
+  // the selections in groups of 8, whose indices are loaded together
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ev[u] = j0 + u < k ? idx[t * k + j0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        const int e = ev[u];
+        int32_t r = -1;
+        if ((unsigned)e < (unsigned)E) {
+          int rank = __popc(mask[e][w] & below);
+          for (int w2 = 0; w2 < w; ++w2) rank += __popc(mask[e][w2]);
+          r = s_base[e] + rank;
+          perm[r] = (int32_t)t;
+        }
+        inv[t * k + j0 + u] = r;
+      }
     }
-    inv[t * k + j] = r;
   }
 }
 
@@ -265,7 +335,8 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
   hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blockcounts, nb, p.E, counts, offsets, blockbase);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blockcounts, nb, p.E, counts, offsets,
+                     blockbase);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockbase, perm,

@@ -43,6 +43,11 @@ CASES = [
     (1024, 64, 256, 8, "bf16", (5,), tuple(range(200, 256))),
     (1025, 64, 256, 8, "bf16", (5,), ()),
     (64, 64, 8, 1, "bf16", (), (7,)),
+    # the scan stages per-block counts in LDS in chunks of 16384: several chunks,
+    # E not a power of two, and k above 8 (selections handled in groups of 8)
+    (40000, 64, 256, 8, "bf16", (3,), tuple(range(10, 30))),
+    (70000, 64, 200, 3, "f32", (), ()),
+    (20000, 64, 64, 12, "bf16", (), (0,)),
 ]
 
 
