@@ -321,12 +321,20 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_fma_kernel(
 int route_splits(const moe_problem_t& p) {
   if (p.dtype != MOE_DTYPE_BF16 || p.E % 8 != 0) return 1;
   const int64_t blocks = ceil_div(p.T, RT);
+  const int nk = p.d_model / RBK;
+  // MOE_ROUTE_SPLITS=<n> forces n splits (clamped to the K steps and the finalize's 64 KB per token)
+  const char* force = getenv("MOE_ROUTE_SPLITS");
+  if (force && force[0]) {
+    int64_t ns = max(1, atoi(force));
+    ns = min(ns, (int64_t)nk);
+    ns = min(ns, (int64_t)(64 * 1024) / (p.E * 4));
+    return (int)max(ns, (int64_t)1);
+  }
   const int cus = device_cus();
   // measured on MI355X: with a quarter of the CUs or more busy the single pass
   // (contraction and selection in one launch) is faster than a split plus the
   // wave-per-token finalize (e.g. 8192 tokens, 64 experts, top-8: 27 against 32 us)
   if (blocks * 4 > cus) return 1;
-  const int nk = p.d_model / RBK;
   int64_t ns = ceil_div(2 * cus, blocks);  // about two router blocks per CU
   ns = min(ns, (int64_t)nk / 4);           // at least four K steps per split
   // partial logits that one finalize wave adds up for its token: at most 64 KB
