@@ -702,11 +702,11 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
 #pragma unroll
     for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ebase = b * (ENT / SUB) + threadIdx.x;
-    // slots in K order, four at a time so that their loads are in flight together
-    for (int si = 0; si < ns; si += 4) {
-      f32x4 v[4][PER];
+    // slots in K order, eight at a time so that their loads are in flight together
+    for (int si = 0; si < ns; si += 8) {
+      f32x4 v[8][PER];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = 0; q4 < 8; ++q4) {
         const int sl = si + q4 < ns ? s_slots[si + q4] : -1;
 #pragma unroll
         for (int u = 0; u < PER; ++u)
@@ -714,7 +714,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
                              : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
+      for (int q4 = 0; q4 < 8; ++q4)
 #pragma unroll
         for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
     }
@@ -858,8 +858,12 @@ int64_t tiles_upper_bound(int64_t R, int N, int E, int bm, int bn) {
   return m_tiles * ceil_div(N, bn);
 }
 
-constexpr int kFixupSub = 8;     // fixup blocks per split tile
-constexpr int kFixupRounds = 4;  // split tiles one fixup block may take in turn
+// fixup blocks per split tile: 16, or fewer when a tile has fewer than 16 x 256 float32x4 entries
+template <int BM, int BN>
+constexpr int fixup_sub() {
+  return BM * BN / 4 / 256 >= 16 ? 16 : BM * BN / 4 / 256;
+}
+constexpr int kFixupRounds = 1;  // split tiles one fixup block may take in turn
 
 template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2, bool FILL = false>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
@@ -876,37 +880,38 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   if (ms && ms[0]) min_steps = max(0, atoi(ms));
   // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
   const int max_rem = FILL ? nb - 1 : nb / 3;
-  // fixup blocks: kFixupSub per split tile, each looping over up to kFixupRounds tiles
+  // fixup blocks: FS per split tile, each looping over up to kFixupRounds tiles
+  constexpr int FS = fixup_sub<BM, BN>();
   const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
-  const unsigned fix_grid = nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * kFixupSub) : 0u;
+  const unsigned fix_grid = nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * FS) : 0u;
   constexpr int NT = WM * WN * 64;
   if (gelu && perm) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true, true>), dim3((unsigned)grid), dim3(NT), 0,
                        s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
                        n_tiles, min_steps, max_rem, perm, a_rows);
     if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else if (perm) {  // the first GEMM without its activation (training keeps U = x W1)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false, true>), dim3((unsigned)grid), dim3(NT),
                        0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
                        n_tiles, min_steps, max_rem, perm, a_rows);
     if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else if (gelu) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
                        n_tiles, min_steps, max_rem, nullptr, R);
     if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, true>), dim3(fix_grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
                        n_tiles, min_steps, max_rem, nullptr, R);
     if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, kFixupSub, false>), dim3(fix_grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
                          offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
   }
   return hipGetLastError();
@@ -921,7 +926,8 @@ hipError_t launch_split_fixup_256(const int32_t* offsets, const float* partials,
                                   int E, int nb, int min_steps, int max_rem, hipStream_t s) {
   const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
   if (nk < min_steps || max_rem <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, 2, 4, kFixupSub, false>), dim3((unsigned)(8 * fix_r * kFixupSub)),
+  constexpr int FS = fixup_sub<256, 256>();
+  hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, 2, 4, FS, false>), dim3((unsigned)(8 * fix_r * FS)),
                      dim3(256), 0, s, offsets, partials, (bf16_bits*)C, R, nk, N, E, (int)ceil_div(N, 256), nb,
                      min_steps, max_rem);
   return hipGetLastError();
