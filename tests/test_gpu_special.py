@@ -97,3 +97,19 @@ def test_one_hip_runtime_in_process(moe):
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
     assert any(moe.lib_path() in line for line in maps.splitlines())
+
+
+@pytest.mark.parametrize("T,k", [(1500, 16), (40, 256)])
+def test_max_experts_large_k(moe, T, k):
+    """256 experts (the limit) with k past the register fast paths: the
+    router's general selection, the permute's selections in groups of 8,
+    and the combine's loop over selections; whole layer and stages agree."""
+    cfg = scaled_config("large_sparse", T=T, d_model=128, d_expert=64, E=256, k=k)
+    announce(f"special E=256 k={k} T={T}")
+    inp = make_inputs(cfg, seed=5, device="cuda")
+    st, ref = run_and_compare(moe, cfg, inp, TOL_BF16)
+    assert np.array_equal(i64(st["counts"]), ref["counts"])
+    layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, inp["x"].dtype)
+    y = layer(inp["x"], inp["w_router"], inp["W1"], inp["W2"], inp["router_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, st["y"])
