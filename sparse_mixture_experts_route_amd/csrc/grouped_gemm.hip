@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
                                                                       int N, int E, int n_tiles, int min_steps,
                                                                       int max_rem,
                                                                       const int32_t* __restrict__ perm,
-                                                                      int64_t a_rows) {
+                                                                      int64_t a_rows, int gm) {
   constexpr int NW = WM * WN;                  // waves
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -207,7 +207,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     tl.e = __builtin_amdgcn_readfirstlane(a0);
     const int local = t - __builtin_amdgcn_readfirstlane(s_tstart[tl.e]);
     const int mt = __builtin_amdgcn_readfirstlane(s_mtiles[tl.e]);
-    const int n_tile = local / mt, m_idx = local - n_tile * mt;
+    int n_tile, m_idx;
+    tile_coords(local, mt, n_tiles, gm, n_tile, m_idx);
     tl.row0 = (int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e]) + (int64_t)m_idx * BM;
     tl.row_end = min((int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e + 1]), R);
     tl.n0 = n_tile * BN;
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
                                                          const float* __restrict__ partials,
                                                          bf16_bits* __restrict__ C, int64_t R, int nk, int N,
                                                          int E, int n_tiles, int nb, int min_steps,
-                                                         int max_rem) {
+                                                         int max_rem, int gm) {
   constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
   constexpr int ENT = BM * BN / 4;           // float32x4 entries per slot
   constexpr int PER = ENT / SUB / 256;       // entries per thread
@@ -693,7 +694,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
       if (s_tstart[mid] <= t) a0 = mid; else a1 = mid;
     }
     const int e = a0, local = t - s_tstart[e], mt = s_mtiles[e];
-    const int n_tile = local / mt, m_idx = local - n_tile * mt;
+    int n_tile, m_idx;
+    tile_coords(local, mt, n_tiles, gm, n_tile, m_idx);
     const int64_t row0 = (int64_t)offsets[e] + (int64_t)m_idx * BM;
     const int64_t row_end = min((int64_t)offsets[e + 1], R);
     const int n0 = n_tile * BN;
@@ -880,6 +882,7 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   if (ms && ms[0]) min_steps = max(0, atoi(ms));
   // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
   const int max_rem = FILL ? nb - 1 : nb / 3;
+  const int gm = group_m();
   // fixup blocks: FS per split tile, each looping over up to kFixupRounds tiles
   constexpr int FS = fixup_sub<BM, BN>();
   const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
@@ -888,31 +891,31 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   if (gelu && perm) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true, true>), dim3((unsigned)grid), dim3(NT), 0,
                        s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, perm, a_rows);
+                       n_tiles, min_steps, max_rem, perm, a_rows, gm);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
   } else if (perm) {  // the first GEMM without its activation (training keeps U = x W1)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false, true>), dim3((unsigned)grid), dim3(NT),
                        0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, perm, a_rows);
+                       n_tiles, min_steps, max_rem, perm, a_rows, gm);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
   } else if (gelu) {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, nullptr, R);
+                       n_tiles, min_steps, max_rem, nullptr, R, gm);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
                        (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, nullptr, R);
+                       n_tiles, min_steps, max_rem, nullptr, R, gm);
     if (fix_grid)
       hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem);
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
   }
   return hipGetLastError();
 }
@@ -929,8 +932,13 @@ hipError_t launch_split_fixup_256(const int32_t* offsets, const float* partials,
   constexpr int FS = fixup_sub<256, 256>();
   hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, 2, 4, FS, false>), dim3((unsigned)(8 * fix_r * FS)),
                      dim3(256), 0, s, offsets, partials, (bf16_bits*)C, R, nk, N, E, (int)ceil_div(N, 256), nb,
-                     min_steps, max_rem);
+                     min_steps, max_rem, group_m());
   return hipGetLastError();
+}
+
+int group_m() {
+  const char* g = getenv("MOE_GEMM_GROUP_M");
+  return g && g[0] ? max(0, atoi(g)) : kGroupM;
 }
 
 int split_min_steps() {

@@ -84,6 +84,7 @@ struct BwdArgs {
   int64_t R, a_rows, b_estride;
   int M, N, K, lda, ldb, E;
   int min_steps, max_rem;  // M-grouped split of the last round (split_leftover)
+  int gm;                  // M-grouped: m-tiles per raster group (tile_coords)
 };
 
 template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
@@ -239,8 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       }
       e = a0;
       const int local = t - s_tstart[e], mtl = s_mtiles[e];
-      nt = local / mtl;
-      mt = local - nt * mtl;
+      tile_coords(local, mtl, n_tiles, args.gm, nt, mt);
       const int64_t g0 = args.offsets ? args.offsets[e] : 0;
       row0 = g0 + (int64_t)mt * kBM;
       row_end = args.offsets ? min((int64_t)args.offsets[e + 1], args.R) : args.R;
@@ -501,6 +501,7 @@ hipError_t launch_bwd_gemm_nt(const bf16_bits* A, int lda, const int32_t* offset
   const int64_t grid = bwd_grid(nt_tiles_ub(R, E, N, offsets != nullptr));
   const int nb = (int)(grid / 8);
   a.min_steps = split_min_steps();
+  a.gm = group_m();
   // the split needs the fixup's tile enumeration (expert groups) and a plain epilogue
   a.max_rem = (partials && offsets && !U) ? nb / 3 : 0;
   hipError_t e = U ? launch<false, false, false, false, EPI_DGELU>(a, grid, s)

@@ -46,6 +46,32 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   __syncthreads();
 }
 
+// Position of tile `local` (0 .. mt * n_tiles - 1) among one expert's mt m-tiles
+// x n_tiles n-tiles. The m-tiles go in groups of gm (the last group holds the
+// rest); inside a group the n-tile is the major index and the m-tile the minor
+// one. A round of consecutive tiles then covers gm row slabs and a few weight
+// slabs, which the blocks of an XCD read together through its L2, also for an
+// expert with many m-tiles (one n-tile major order over all of them would put
+// up to a whole round of row slabs next to a single weight slab).
+// gm <= 0 or mt <= gm: one group.
+__host__ __device__ __forceinline__ void tile_coords(int local, int mt, int n_tiles, int gm, int& nt, int& m) {
+  if (gm <= 0 || mt <= gm) {
+    nt = local / mt;
+    m = local - nt * mt;
+    return;
+  }
+  const int per = gm * n_tiles, full = mt / gm;
+  const int grp = local / per, in = local - grp * per;
+  const int g = grp < full ? gm : mt - full * gm;
+  nt = in / g;
+  m = grp * gm + (in - nt * g);
+}
+
+// m-tiles per raster group of the grouped GEMMs (tile_coords); MOE_GEMM_GROUP_M
+// overrides it (0: one group per expert).
+constexpr int kGroupM = 8;
+int group_m();
+
 // Work of one block of a persistent launch over `tiles` tiles of `nk` K steps
 // shared by `nb` blocks (index j): `full` whole tiles (tiles j, j + nb, ...),
 // then units [s0, s1) of the remaining rem * nk (tile, K step) units, counted

@@ -112,6 +112,30 @@ def test_backward_split_last_round(moe, blocks):
         assert err <= TOL_BF16, key
 
 
+@pytest.mark.parametrize("blocks", [24, 64])
+def test_backward_raster_groups_do_not_change_results(moe, blocks):
+    """The row-grouped backward GEMMs and their split fixup deal an expert's
+    tiles in raster groups of MOE_GEMM_GROUP_M m-tiles: every gradient equals
+    the one-group run bit for bit."""
+    import os
+    cfg = scaled_config("skewed", T=12000, d_model=512, E=8, k=2, d_expert=256, suffix="bwdgm")
+    announce(f"backward raster groups blocks={blocks}")
+    inp = make_inputs(cfg, seed=8, device="cuda")
+    dy = make_dense((cfg.T, cfg.d_model), 1.0, seed=8, tag=9, device="cuda")
+    res = {}
+    for gm in ("0", "8"):
+        env = {"MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_SPLIT_MIN_STEPS": "0", "MOE_GEMM_GROUP_M": gm}
+        os.environ.update(env)
+        try:
+            _, g = run_train(moe, cfg, inp, dy)
+        finally:
+            for key in env:
+                del os.environ[key]
+        res[gm] = {key: g[key].clone() for key in ("dx", "dw_router", "dW1", "dW2")}
+    for key in res["0"]:
+        assert torch.equal(res["0"][key], res["8"][key]), key
+
+
 def test_backward_repeatable_and_workspace_reuse(moe):
     """Two backward calls on one training workspace give identical results (no
     atomics, fixed summation orders), and a second training step reuses it."""

@@ -155,3 +155,40 @@ def test_gather_path_matches_permuted_copy(moe, tile, split0):
     for name, t in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
         assert torch.equal(t, st[name]), name
     assert torch.equal(y_perm, st["y_perm"])
+
+
+@pytest.mark.parametrize("blocks,split0", [(24, True), (64, False), (256, False)])
+def test_raster_groups_do_not_change_results(moe, blocks, split0):
+    """The order in which an expert's tiles are dealt to blocks (m-tiles in
+    raster groups of MOE_GEMM_GROUP_M, or one group) changes no sum: the
+    outputs are equal bit for bit, with experts of many m-tiles, split
+    leftover tiles and the row-gathering first GEMM."""
+    R, d, de, E = 9000, 256, 320, 3
+    announce(f"ffn raster groups blocks={blocks} split0={split0}")
+    x = make_dense((R, d), 1.0, seed=12, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=12, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=12, tag=3, device="cuda")
+    off = make_group_offsets(E, R, seed=12).cuda()
+    perm = torch.arange(R, dtype=torch.int32, device="cuda")
+    p = moe.make_problem(R, d, E, 1, de, "bf16")
+    out = {}
+    for gm in ("0", "1", "3", "8"):
+        env = {"MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_GROUP_M": gm}
+        if split0:
+            env["MOE_GEMM_SPLIT_MIN_STEPS"] = "0"
+        os.environ.update(env)
+        try:
+            y = run_ffn(moe, R, d, de, E, "bf16", x, off, W1, W2)
+            ws = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device="cuda")
+            yg = torch.full_like(y, float("nan"))
+            moe.moe_grouped_ffn_gather(p, x, perm, off, W1, W2, yg, ws)
+            torch.cuda.synchronize()
+        finally:
+            for k in env:
+                del os.environ[k]
+        out[gm] = (y, yg)
+    for gm in ("1", "3", "8"):
+        assert torch.equal(out[gm][0], out["0"][0]), gm
+        assert torch.equal(out[gm][1], out["0"][1]), gm
+    ref = oracle_ffn("bf16", x, off.cpu(), W1, W2)
+    assert rel_err(f64(out["8"][0]), ref) <= TOL_BF16
