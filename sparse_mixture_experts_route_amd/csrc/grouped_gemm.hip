@@ -811,14 +811,15 @@ constexpr int kMaxCUs = 256;
 }  // namespace
 
 int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
+  // initialised once, thread-safely (a function-local static); callers on
+  // several threads never see a partial or unclamped value
+  static const int cus = [] {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cus = min(max(cus, 8), kMaxCUs);
-  }
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return min(max(n, 8), kMaxCUs);
+  }();
   return cus;
 }
 

@@ -33,7 +33,11 @@
 // as the forward kernel); K-grouped launches run E x (M / 256) x (N / 256)
 // tiles, each reducing over its expert's rows (zero rows: the tile stores
 // zeros), experts taken in order of decreasing row count so that the long
-// tiles of hot experts start first. The A operand of a K-grouped launch may
+// tiles of hot experts start first. When a hot expert's reduction is much
+// longer than a block's fair share of the launch, its tiles are cut into
+// chunks of K steps (kgroup_schedule): each chunk writes float32 partial sums
+// and kgroup_fixup_kernel adds them in chunk order (deterministic, no
+// atomics). The A operand of a K-grouped launch may
 // be gathered: row r read as row perm[r] of a [a_rows, M] matrix (dW1 reads
 // the tokens straight from x). The epilogue stages bf16 results through LDS
 // and writes whole row segments; EPI_DGELU multiplies by GELU_tanh'(U) at the
@@ -71,6 +75,86 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
   return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * c * fmaf(3.0f * a, u * u, 1.0f);
 }
 
+// K-grouped schedule (both the GEMM kernel and its fixup derive it, the same
+// way, from the row groups): experts by decreasing row count (ties: lower
+// index first) in order[]; with partial-sum slots available (max_slots > 0),
+// an expert of nk K steps is cut into c = ceil(nk / L) chunks when nk > L, with
+// L = max(kMinChunk, ceil(W / (4 nb))) doubled until the chunked experts' items
+// fit in max_slots (W: the K steps of all tiles, nb: blocks of the launch).
+// Items: rank by rank, chunk-major, then tile; ibase[r] = first item of rank
+// r, ibase[E] = items. The chunked experts rank first, so their items are the
+// partial-sum slots 0 ... Returns L (huge when nothing is cut).
+constexpr int kMinChunk = 16;
+template <typename Grp>
+__device__ int kgroup_schedule(Grp grp, int E, int per, int nb, int max_slots, int* order, int* chunks,
+                               int* ibase) {
+  __shared__ int s_L;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int64_t c = grp(e + 1) - grp(e);
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const int64_t cf = grp(f + 1) - grp(f);
+      rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    }
+    order[rank] = e;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    int64_t nk[4];
+    int64_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lane * 4 + i;
+      nk[i] = r < E ? ceil_div(max(grp(order[r] + 1) - grp(order[r]), (int64_t)0), kBK) : 0;
+      w += nk[i] * per;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o, kWave);
+    int64_t L = max((int64_t)kMinChunk, ceil_div(w, (int64_t)4 * nb));
+    if (max_slots <= 0) L = INT32_MAX / 2;
+    for (;;) {  // coarser chunks until the partial sums fit
+      int64_t slots = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = ceil_div(nk[i], L);
+        slots += c > 1 ? c * per : 0;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) slots += __shfl_xor(slots, o, kWave);
+      if (slots <= max_slots || L >= INT32_MAX / 4) break;
+      L *= 2;
+    }
+    int c[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = lane * 4 + i < E ? (int)max((int64_t)1, ceil_div(nk[i], L)) : 0;
+      local += c[i] * per;
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lane * 4 + i;
+      if (r < E) {
+        chunks[r] = c[i];
+        ibase[r] = run;
+      }
+      run += c[i] * per;
+    }
+    if (lane == kWave - 1) ibase[E] = incl;
+    if (lane == 0) s_L = (int)L;
+  }
+  __syncthreads();
+  return s_L;
+}
+
 struct BwdArgs {
   const bf16_bits* A;   // M-grouped: [R, lda] rows; K-grouped: [rows, lda] (or [a_rows, lda] gathered)
   const bf16_bits* B;   // M-grouped: expert e at B + e * b_estride, [N, ldb] rows (K-contiguous);
@@ -85,6 +169,7 @@ struct BwdArgs {
   int M, N, K, lda, ldb, E;
   int min_steps, max_rem;  // M-grouped split of the last round (split_leftover)
   int gm;                  // M-grouped: m-tiles per raster group (tile_coords)
+  int kslots;              // K-grouped: partial-sum slots for chunked tiles (0: no chunks)
 };
 
 template <bool KGROUP, bool A_MN, bool B_MN, bool GATHER_A, int EPI>
@@ -93,6 +178,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   __shared__ int s_tstart[257];
   __shared__ int s_mtiles[256];
   __shared__ int s_order[256];
+  __shared__ int s_chunks[256];
+  __shared__ int s_ibase[257];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -105,20 +192,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   const int n_tiles = (int)ceil_div(args.N, kBN);
   const int m_fixed = (int)ceil_div(args.M, kBM);  // K-grouped: m tiles per expert
 
-  int total;
+  int total, kL = 0;
   if constexpr (KGROUP) {
-    // experts by decreasing row count (ties: lower index first)
-    for (int e = tid; e < E; e += kThreads) {
-      const int64_t c = grp(e + 1) - grp(e);
-      int rank = 0;
-      for (int f = 0; f < E; ++f) {
-        const int64_t cf = grp(f + 1) - grp(f);
-        rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
-      }
-      s_order[rank] = e;
-    }
-    __syncthreads();
-    total = E * m_fixed * n_tiles;
+    kL = kgroup_schedule(grp, E, m_fixed * n_tiles, (int)gridDim.x, args.partials ? args.kslots : 0, s_order,
+                         s_chunks, s_ibase);
+    total = s_ibase[E];
   } else {
     if (args.offsets) {
       build_tile_list<kBM>(args.offsets, E, args.R, n_tiles, s_tstart, s_mtiles);
@@ -225,13 +303,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
     int e, mt, nt;
     int64_t row0, row_end;  // M-grouped: rows of A and C; K-grouped: rows of the expert (K range)
     if constexpr (KGROUP) {
+      // rank r with ibase[r] <= t < ibase[r + 1]; chunk ch of its reduction, tile lt
       const int per = m_fixed * n_tiles;
-      e = s_order[t / per];
-      const int local = t - (t / per) * per;
-      nt = local / m_fixed;
-      mt = local - nt * m_fixed;
+      int a0 = 0, a1 = E;
+      while (a1 - a0 > 1) {
+        const int mid = (a0 + a1) >> 1;
+        if (s_ibase[mid] <= t) a0 = mid; else a1 = mid;
+      }
+      e = s_order[a0];
+      const int local = t - s_ibase[a0], ch = local / per, lt = local - ch * per;
+      nt = lt / m_fixed;
+      mt = lt - nt * m_fixed;
       row0 = grp(e);
       row_end = grp(e + 1);
+      if (s_chunks[a0] > 1) {  // a chunk: float32 partial sums to slot t
+        row0 += (int64_t)ch * kL * kBK;
+        row_end = min(row_end, row0 + (int64_t)kL * kBK);
+        slot = t;
+      }
     } else {
       int a0 = 0, a1 = E;
       while (a1 - a0 > 1) {
@@ -427,6 +516,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
   }
 }
 
+// Completion of the chunked tiles of a K-grouped launch: the schedule of the
+// GEMM kernel (kgroup_schedule with the launch's block count nb), then, per
+// (chunked tile, part of kFixParts), the tile's partial-sum slots added in
+// chunk order, rounded to bf16 and stored to C_e (row and column bounds M, N).
+constexpr int kFixParts = 16;
+__global__ __launch_bounds__(256) void kgroup_fixup_kernel(BwdArgs args, int nb) {
+  __shared__ int s_order[256];
+  __shared__ int s_chunks[256];
+  __shared__ int s_ibase[257];
+  const int E = args.E;
+  auto grp = [&](int e) -> int64_t { return args.offsets ? (int64_t)args.offsets[e] : args.R * e / E; };
+  const int n_tiles = (int)ceil_div(args.N, kBN), m_fixed = (int)ceil_div(args.M, kBM), per = m_fixed * n_tiles;
+  kgroup_schedule(grp, E, per, nb, args.kslots, s_order, s_chunks, s_ibase);
+  int n_chunked = 0;  // the chunked experts rank first
+  while (n_chunked < E && s_chunks[n_chunked] > 1) ++n_chunked;
+  constexpr int ENT = kBM * kBN / 4;         // float32x4 entries per slot
+  constexpr int PER = ENT / kFixParts / 256;  // entries per thread and unit
+  const int units = n_chunked * per * kFixParts;
+  for (int w = blockIdx.x; w < units; w += gridDim.x) {
+    const int u = w / kFixParts, part = w - u * kFixParts;
+    const int r = u / per, lt = u - r * per;
+    const int e = s_order[r], c = s_chunks[r];
+    const int nt = lt / m_fixed, mt = lt - nt * m_fixed;
+    const int ebase = part * (ENT / kFixParts) + threadIdx.x;
+    f32x4 acc[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < c; ++ch) {
+      const f32x4* src = (const f32x4*)(args.partials + (int64_t)(s_ibase[r] + ch * per + lt) * (kBM * kBN));
+#pragma unroll
+      for (int q = 0; q < PER; ++q) acc[q] += src[ebase + q * 256];
+    }
+    bf16_bits* const Cb = args.C + (int64_t)e * args.M * args.N;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
+      const int en = ebase + q * 256, grp_ = en / kThreads, tt = en % kThreads;
+      const int mi = grp_ / (kTN * 4), ni = (grp_ / 4) % kTN, gq = grp_ % 4;
+      const int wave = tt / kWave, lane = tt % kWave;
+      const int row = mt * kBM + (wave / kWN) * kWTM + mi * 32 + (lane & 31);
+      const int col = nt * kBN + (wave % kWN) * kWTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
+      if (row >= args.M || col >= args.N) continue;
+      u32x2 o;
+      o[0] = pack_bf16x2(acc[q][0], acc[q][1]);
+      o[1] = pack_bf16x2(acc[q][2], acc[q][3]);
+      *(u32x2*)(Cb + (int64_t)row * args.N + col) = o;
+    }
+  }
+}
+
 // persistent grid: one block per CU at most, a multiple of 8 (the XCD ranges);
 // MOE_GEMM_MAX_BLOCKS=<n> lowers the cap as for the forward GEMMs (several
 // rounds on small problems: exercises the split of the last round)
@@ -512,7 +651,7 @@ hipError_t launch_bwd_gemm_nt(const bf16_bits* A, int lda, const int32_t* offset
 
 hipError_t launch_bwd_gemm_tn(const bf16_bits* A, int lda, const int32_t* perm, int64_t a_rows,
                               const int32_t* offsets, int64_t R, int E, const bf16_bits* B, int ldb, bf16_bits* C,
-                              int M, int N, hipStream_t s) {
+                              int M, int N, float* partials, hipStream_t s) {
   if (M <= 0 || N <= 0 || lda % 8 || ldb % 8 || M % 8 || N % 8) return hipErrorInvalidValue;
   if ((perm ? a_rows : R) * (int64_t)lda * 2 >= INT32_MAX || R * (int64_t)ldb * 2 >= INT32_MAX)
     return hipErrorInvalidValue;
@@ -521,11 +660,23 @@ hipError_t launch_bwd_gemm_tn(const bf16_bits* A, int lda, const int32_t* perm, 
   a.R = R; a.a_rows = a_rows; a.b_estride = 0;
   a.M = M; a.N = N; a.K = 0; a.lda = lda; a.ldb = ldb; a.E = E;
   a.min_steps = 0; a.max_rem = 0;
+  // chunked tiles of hot experts need the partial-sum slots (kgroup_slots)
+  a.partials = offsets ? partials : nullptr;
+  a.kslots = a.partials ? kgroup_slots() : 0;
   const int64_t tiles = (int64_t)E * ceil_div(M, kBM) * ceil_div(N, kBN);
   const int64_t grid = min(tiles, (int64_t)device_cus());
   if (tiles <= 0) return hipSuccess;
-  if (perm) return launch<true, true, true, true, EPI_PLAIN>(a, grid, s);
-  return launch<true, true, true, false, EPI_PLAIN>(a, grid, s);
+  hipError_t e = perm ? launch<true, true, true, true, EPI_PLAIN>(a, grid, s)
+                      : launch<true, true, true, false, EPI_PLAIN>(a, grid, s);
+  if (e != hipSuccess || !a.partials) return e;
+  hipLaunchKernelGGL(kgroup_fixup_kernel, dim3((unsigned)device_cus()), dim3(256), 0, s, a, (int)grid);
+  return hipGetLastError();
+}
+
+int kgroup_slots() {
+  // MOE_BWD_KGROUP_SLOTS=<n> lowers the slot count (0: never cut a tile's reduction)
+  const char* v = getenv("MOE_BWD_KGROUP_SLOTS");
+  return v && v[0] ? min(max(0, atoi(v)), kKGroupSlots) : kKGroupSlots;  // the workspace holds kKGroupSlots
 }
 
 }  // namespace moe

@@ -80,7 +80,12 @@ hipError_t launch_bwd_gemm_nt(const uint16_t* A, int lda, const int32_t* offsets
 // C_e = C + e * M * N as [M, N]. Experts without rows get zeros.
 hipError_t launch_bwd_gemm_tn(const uint16_t* A, int lda, const int32_t* perm, int64_t a_rows,
                               const int32_t* offsets, int64_t R, int E, const uint16_t* B, int ldb, uint16_t* C,
-                              int M, int N, hipStream_t s);
+                              int M, int N, float* partials, hipStream_t s);
+// Partial-sum slots (256 x 256 float32 each) that the K-grouped launches with
+// expert row groups may use to cut hot experts' reductions into chunks; the
+// workspace holds kKGroupSlots of them.
+constexpr int kKGroupSlots = 256;
+int kgroup_slots();
 // Split-tile fixup of an 8-wave 256 x 256 row-grouped launch (no activation),
 // and the split threshold in K steps (MOE_GEMM_SPLIT_MIN_STEPS overrides it).
 hipError_t launch_split_fixup_256(const int32_t* offsets, const float* partials, uint16_t* C, int64_t R, int nk, int N,

@@ -132,9 +132,11 @@ TrainWs carve_train(Carver& c, const moe_problem_t& p) {
   w.y_perm = c.take<uint16_t>(R * p.d_model);
   w.pw = carve_permute(c, p);
   w.route_part = carve_route(c, p);
+  // one region for the split partial sums of every GEMM of the step, used in turn
   const size_t pb = std::max({moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_model, p.d_expert, p.E),
                               moe::grouped_gemm_partials_bytes(p.dtype, (int64_t)R, p.d_expert, p.d_model, p.E),
-                              moe::bwd_partials_bytes((int64_t)R, p.E, p.d_model)});
+                              moe::bwd_partials_bytes((int64_t)R, p.E, p.d_model),
+                              (size_t)moe::kKGroupSlots * 256 * 256 * sizeof(float)});
   w.partials = c.take<float>(pb / sizeof(float));
   w.dwr_part = c.take<uint16_t>((size_t)moe::bwd_router_splits(p.T, p.d_model, p.E) * p.d_model * p.E);
   w.dYp = c.take<uint16_t>(R * p.d_model);
@@ -424,10 +426,10 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   // dW2_e = H^T dYp, dW1_e = x[perm]^T dU over each expert's rows
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_tn((cb)w.H, de, nullptr, R, w.offsets, R, p->E, (cb)w.dYp, d, (uint16_t*)dW2, de, d,
-                                s);
+                                w.partials, s);
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_tn((cb)x, d, w.perm, p->T, w.offsets, R, p->E, (cb)w.dU, de, (uint16_t*)dW1, d, de,
-                                s);
+                                w.partials, s);
   // router: dx_r = dlogit W_r^T, dW_r = x^T dlogit (one group of T rows)
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_nt(w.dlogit_b, Ep, nullptr, p->T, 1, (cb)w_router, p->E, 0, (uint16_t*)w.dxr, d, Ep,
@@ -437,7 +439,7 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   const int splits = moe::bwd_router_splits(p->T, d, p->E);
   if (e == hipSuccess)
     e = moe::launch_bwd_gemm_tn((cb)x, d, nullptr, p->T, nullptr, p->T, splits, w.dlogit_b, Ep,
-                                splits > 1 ? w.dwr_part : (uint16_t*)dw_router, d, p->E, s);
+                                splits > 1 ? w.dwr_part : (uint16_t*)dw_router, d, p->E, nullptr, s);
   if (e == hipSuccess && splits > 1)
     e = moe::launch_sum_splits(w.dwr_part, splits, (int64_t)d * p->E, (uint16_t*)dw_router, s);
   if (e == hipSuccess) e = moe::launch_bwd_dx(*p, w.dXp, w.inv, w.dxr, dx, s);

@@ -136,6 +136,41 @@ def test_backward_raster_groups_do_not_change_results(moe, blocks):
         assert torch.equal(res["0"][key], res["8"][key]), key
 
 
+def test_backward_chunked_hot_experts(moe):
+    """Skewed routing: the weight-gradient reductions of the two hot experts
+    are cut into chunks of K steps whose float32 partial sums a fixup adds in
+    chunk order. The gradients match the oracle, repeat bit for bit, and differ
+    (in rounding only) from the run that keeps every reduction whole, which
+    shows that the chunked path ran."""
+    import os
+    cfg = scaled_config("skewed", T=2048, d_model=256, E=16, k=4, d_expert=256, suffix="chunk")
+    announce("backward chunked hot experts")
+    inp = make_inputs(cfg, seed=10, device="cuda")
+    dy = make_dense((cfg.T, cfg.d_model), 1.0, seed=10, tag=9, device="cuda")
+    runs = {}
+    for name, env in (("chunked", {}), ("chunked2", {}), ("whole", {"MOE_BWD_KGROUP_SLOTS": "0"})):
+        os.environ.update(env)
+        try:
+            _, g = run_train(moe, cfg, inp, dy)
+        finally:
+            for key in env:
+                del os.environ[key]
+        runs[name] = {key: g[key].clone() for key in ("dx", "dw_router", "dW1", "dW2")}
+    for key in runs["chunked"]:
+        assert torch.equal(runs["chunked"][key], runs["chunked2"][key]), key
+    assert not (torch.equal(runs["chunked"]["dW1"], runs["whole"]["dW1"])
+                and torch.equal(runs["chunked"]["dW2"], runs["whole"]["dW2"]))
+    h = {kk: host_array(v) for kk, v in inp.items()}
+    ref = oracle.backward(h["x"], h["w_router"], h["router_bias"], h["W1"], h["W2"], cfg.k, cfg.dtype,
+                          host_array(dy))
+    assert not ref["near_tie"].any()
+    for name in ("chunked", "whole"):
+        for key in ("dx", "dw_router", "dW1", "dW2"):
+            err = rel_err(f64(runs[name][key]), ref[key])
+            print(f"{name} {key}: rel err {err:.3e}")
+            assert err <= TOL_BF16, (name, key)
+
+
 def test_backward_repeatable_and_workspace_reuse(moe):
     """Two backward calls on one training workspace give identical results (no
     atomics, fixed summation orders), and a second training step reuses it."""
