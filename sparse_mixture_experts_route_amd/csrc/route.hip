@@ -35,11 +35,21 @@ namespace {
 
 // ---------------------------------------------------------------- matrix-core path
 
-constexpr int RT = 64;  // tokens per block
+constexpr int RT64 = 64;  // tokens per block (RT32: a block of 32 tokens and two waves)
+constexpr int RT32 = 32;
 constexpr int RBK = 64; // K step
 
-// Block: RT tokens x EP experts (E padded), four waves in a 2x2 grid, each
-// 32 tokens x EP/2 experts. Operands stream HBM -> LDS through a ring of S
+// true when c ^ m < n for every chunk c < n and mask m' <= m (all XOR masks
+// the swizzle uses), i.e. the XOR permutes the row's n chunks
+constexpr bool xor_stays_in_row(int n, int m) {
+  for (int mm = 0; mm <= m; ++mm)
+    for (int c = 0; c < n; ++c)
+      if ((c ^ mm) >= n) return false;
+  return true;
+}
+
+// Block: RT tokens x EP experts (E padded), RT / 16 waves in a (RT / 32) x 2
+// grid, each 32 tokens x EP/2 experts. Operands stream HBM -> LDS through a ring of S
 // stages with direct-to-LDS loads (x rows K-contiguous, chunk XOR-swizzled;
 // w_router rows E-contiguous, read with the transposing LDS read), one
 // barrier per K step, the fragments of the next K sub-step read while the
@@ -49,21 +59,25 @@ constexpr int RBK = 64; // K step
 // Split over d_model (gridDim.y = nsplit > 1): block (b, s) takes K steps
 // [s nk / nsplit, (s+1) nk / nsplit) and writes its float32 partial logits
 // (no bias) to part[s][t][e]; route_finalize_kernel adds them up and selects.
-template <int EP, int S>
-__global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __restrict__ x,
+template <int EP, int S, int RT = 64>
+__global__ __launch_bounds__(RT * 4) void route_mfma_kernel(const bf16_bits* __restrict__ x,
                                                          const bf16_bits* __restrict__ wr,
                                                          const float* __restrict__ bias, float* __restrict__ logits,
                                                          int32_t* __restrict__ idx, float* __restrict__ gate,
                                                          float* __restrict__ part, int64_t T, int d, int E_real,
                                                          int k) {
-  constexpr int NW = 4;
+  constexpr int NW = RT / 16;                 // 2 x 2 waves for 64 tokens, 1 x 2 for 32
+  static_assert(RT == 64 || RT == 32, "router block of 64 or 32 tokens");
   constexpr int WTN = EP / 2, TN = WTN / 32;  // experts per wave, 32-wide MFMA tiles
   constexpr int KS = RBK / 16;                // MFMA K sub-steps per stage
   constexpr int A_ROW = RBK * 2, A_STAGE = RT * A_ROW;
   constexpr int B_ROW = EP * 2, B_SLOTS = EP / 8, B_STAGE = RBK * B_ROW;
   constexpr int STAGE = A_STAGE + B_STAGE;
   constexpr int A_LD = A_STAGE / 1024 / NW, B_LD = B_STAGE / 1024 / NW, NL = A_LD + B_LD;
-  constexpr int BSW = B_SLOTS >= 16 ? 4 : 2;  // B chunk swizzle: XOR by BSW * (k & 3)
+  // B chunk swizzle: XOR by BSW * (k & 3), a permutation of the row's chunks
+  // (24 chunks, E padded to 192, only take XORs below 8)
+  constexpr int BSW = B_SLOTS % 16 == 0 ? 4 : 2;
+  static_assert(xor_stays_in_row(B_SLOTS, BSW * 3), "router B swizzle leaves the row");
   constexpr int LG_ROW = EP + 1;              // float32 logits row in the epilogue
   constexpr int RING = S * STAGE;
   constexpr int SMEM = RING > RT * LG_ROW * 4 ? RING : RT * LG_ROW * 4;
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16_bits* __rest
     return;
   }
   if (k <= kTopkFast) {
-    select_topk_block<RT>(lg, LG_ROW, t0, T, E_real, k, idx, gate);
+    select_topk_block<RT, RT * 4>(lg, LG_ROW, t0, T, E_real, k, idx, gate);
     if (logits)  // rows of the block, coalesced
       for (int i = tid; i < RT * E_real; i += NW * kWave) {
         const int r = i / E_real, e = i - r * E_real;
@@ -318,9 +332,40 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_fma_kernel(
 
 }  // namespace
 
+// Tokens per matrix-core router block. MOE_ROUTE_RT=32|64 forces a size.
+int route_rt(const moe_problem_t& p) {
+  const char* force = getenv("MOE_ROUTE_RT");
+  if (force && force[0]) return atoi(force) == 32 ? RT32 : RT64;
+  // 32-token blocks where 64-token blocks would leave CUs idle but are too
+  // many to split over d_model (a quarter to all of the CUs), and the router
+  // tile is narrow enough that twice the w_router reads per token stay cheap.
+  // Measured on MI355X: 8192 tokens x 64 experts x 2048, 19.1 against 21.2 us;
+  // 4096 tokens x 8 experts (split) and 16384 tokens keep 64.
+  const int64_t b64 = ceil_div(p.T, RT64);
+  const int cus = device_cus();
+  if (p.E <= 128 && b64 * 4 > cus && b64 < cus) return RT32;
+  return RT64;
+}
+
+// the router kernel for the padded expert count and block size
+template <typename Go>
+hipError_t route_dispatch(const moe_problem_t& p, Go go) {
+  const bool small = route_rt(p) == RT32;
+  switch ((p.E + 63) / 64 * 64) {
+    case 64:
+      return small ? go(route_mfma_kernel<64, 4, RT32>, RT32) : go(route_mfma_kernel<64, 4>, RT64);
+    case 128:
+      return small ? go(route_mfma_kernel<128, 4, RT32>, RT32) : go(route_mfma_kernel<128, 4>, RT64);
+    case 192:
+      return small ? go(route_mfma_kernel<192, 3, RT32>, RT32) : go(route_mfma_kernel<192, 3>, RT64);
+    default:
+      return small ? go(route_mfma_kernel<256, 3, RT32>, RT32) : go(route_mfma_kernel<256, 3>, RT64);
+  }
+}
+
 int route_splits(const moe_problem_t& p) {
   if (p.dtype != MOE_DTYPE_BF16 || p.E % 8 != 0) return 1;
-  const int64_t blocks = ceil_div(p.T, RT);
+  const int64_t blocks = ceil_div(p.T, route_rt(p));
   const int nk = p.d_model / RBK;
   // MOE_ROUTE_SPLITS=<n> forces n splits (clamped to the K steps and the finalize's 64 KB per token)
   const char* force = getenv("MOE_ROUTE_SPLITS");
@@ -351,54 +396,31 @@ hipError_t launch_route_partials(const moe_problem_t& p, const void* x, const vo
                                  hipStream_t s) {
   const int ns = route_splits(p);
   if (ns <= 1 || !part) return hipErrorInvalidValue;
-  const int64_t blocks = ceil_div(p.T, RT);
   const bf16_bits* xb = (const bf16_bits*)x;
   const bf16_bits* wb = (const bf16_bits*)w_router;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ns), dim3(256), 0, s, xb, wb, nullptr, nullptr,
-                       nullptr, nullptr, part, p.T, p.d_model, p.E, p.k);
+  return route_dispatch(p, [&](auto kern, int rt) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(p.T, rt), (unsigned)ns), dim3(rt * 4), 0, s, xb, wb, nullptr,
+                       nullptr, nullptr, nullptr, part, p.T, p.d_model, p.E, p.k);
     return hipGetLastError();
-  };
-  switch ((p.E + 63) / 64 * 64) {
-    case 64:
-      return go(route_mfma_kernel<64, 4>);
-    case 128:
-      return go(route_mfma_kernel<128, 4>);
-    case 192:
-      return go(route_mfma_kernel<192, 3>);
-    default:
-      return go(route_mfma_kernel<256, 3>);
-  }
+  });
 }
 
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* w_router, const float* bias,
                         float* logits, int32_t* idx, float* gate, float* part, hipStream_t s) {
   if (p.dtype == MOE_DTYPE_BF16 && p.E % 8 == 0) {
-    const int64_t blocks = ceil_div(p.T, RT);
     const bf16_bits* xb = (const bf16_bits*)x;
     const bf16_bits* wb = (const bf16_bits*)w_router;
-    const int ep = (p.E + 63) / 64 * 64;  // padded expert count
     const int ns = part ? route_splits(p) : 1;
-    auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ns), dim3(256), 0, s, xb, wb, bias, logits, idx,
-                         gate, part, p.T, p.d_model, p.E, p.k);
+    // ring stages: 4 while a stage is small, 3 for the widest tiles (LDS: S * (RT * 128 + 128 * EP B))
+    return route_dispatch(p, [&](auto kern, int rt) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(p.T, rt), (unsigned)ns), dim3(rt * 4), 0, s, xb, wb, bias,
+                         logits, idx, gate, part, p.T, p.d_model, p.E, p.k);
       if (ns > 1)
         hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)ceil_div(p.T, kFinalizeWaves)),
                            dim3(kFinalizeWaves * kWave), 0, s,
                            (const float*)part, ns, bias, logits, idx, gate, p.T, p.E, p.k);
       return hipGetLastError();
-    };
-    // ring stages: 4 while a stage is small, 3 for the widest tiles (LDS: S * (8 KB + 128 * EP B))
-    switch (ep) {
-      case 64:
-        return go(route_mfma_kernel<64, 4>);
-      case 128:
-        return go(route_mfma_kernel<128, 4>);
-      case 192:
-        return go(route_mfma_kernel<192, 3>);
-      default:
-        return go(route_mfma_kernel<256, 3>);
-    }
+    });
   }
   const int64_t blocks = ceil_div(p.T, kRouteWaves);
   if (p.dtype == MOE_DTYPE_BF16) {

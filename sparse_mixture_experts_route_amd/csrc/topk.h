@@ -68,10 +68,10 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-template <int RT_>
+template <int RT_, int NT_ = 256>
 __device__ __forceinline__ void select_topk_block(const float* lg, int ld, int64_t t0, int64_t T, int E, int k,
                                                   int32_t* __restrict__ idx, float* __restrict__ gate) {
-  static_assert(RT_ * 4 == 256, "four threads per token, 256 threads");
+  static_assert(RT_ * 4 == NT_, "four threads per token");
   const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
   const float* row = lg + r * ld;
   uint64_t top[kTopkFast];

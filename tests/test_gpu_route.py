@@ -128,3 +128,36 @@ def test_route_zero_router_ties_to_lowest_index(moe):
     assert np.all(logits == 0)
     assert np.array_equal(idx, np.tile(np.arange(cfg.k), (cfg.T, 1)))
     assert np.all(gate == np.float32(1.0 / cfg.E))
+
+
+@pytest.mark.parametrize("rt", ["32", "64"])
+@pytest.mark.parametrize("name,T,d,E,k", [
+    ("fine_grained", 517, 2048, 64, 6),
+    ("skewed", 1000, 1024, 128, 8),
+    ("large_sparse", 95, 1024, 256, 8),
+    ("fine_grained", 77, 512, 192, 12),
+    ("fine_grained", 300, 1024, 136, 4),
+    ("skewed", 129, 768, 160, 2),
+])
+def test_route_block_sizes_bit_exact(moe, rt, name, T, d, E, k):
+    """The matrix-core router's block of 32 or 64 tokens (MOE_ROUTE_RT): on
+    inputs whose logits are exact, logits and indices equal the oracle's bit
+    for bit, with ragged last blocks, every padded expert width (64 .. 256,
+    also 192, whose w_router rows hold 24 LDS chunks) and k beyond the
+    register top-k list."""
+    import os
+    cfg = scaled_config(name, T=T, d_model=d, E=E, k=k)
+    announce(f"route block {rt} {name} T={T} d={d} E={E} k={k}")
+    inp = make_exact_router_inputs(cfg, seed=4, device="cuda", bias=True, tie_group=3)
+    os.environ["MOE_ROUTE_RT"] = rt
+    try:
+        for via in ("moe_route", "moe_route_ws"):
+            logits, idx, gate = run_route(moe, cfg, inp["x"], inp["w_router"], inp["router_bias"], via)
+            ref = oracle.route(oracle.decode(host_array(inp["x"]), cfg.dtype),
+                               oracle.decode(host_array(inp["w_router"]), cfg.dtype),
+                               host_array(inp["router_bias"]), cfg.k)
+            assert np.array_equal(logits, ref["logits"]), via
+            assert np.array_equal(idx, ref["idx"]), via
+            np.testing.assert_allclose(gate, ref["gate"], rtol=32 * U32, atol=0)
+    finally:
+        del os.environ["MOE_ROUTE_RT"]
