@@ -48,3 +48,30 @@ def test_combine_skips_ignored_selections(moe):
     moe.moe_combine(moe.make_problem(T, d, E, k, 64, "f32"), y_perm, inv, gate, y)
     torch.cuda.synchronize()
     assert torch.equal(y, 0.5 * y_perm[0::2])
+
+
+@pytest.mark.parametrize("T,d,k", [(333, 2048, 2), (1000, 256, 8), (257, 7168, 8), (40, 1088, 12)])
+def test_combine_streaming_accesses_match(moe, T, d, k):
+    """The non-temporal variant (chosen for large y_perm) and the plain one do
+    the same arithmetic: bit-equal outputs, and the oracle's within tolerance."""
+    import os
+    E = 64
+    announce(f"combine streaming T={T} d={d} k={k}")
+    idx = make_routing_table(T, E, k, seed=11)
+    inv = torch.from_numpy(oracle.permute(idx.numpy(), E)["inv"]).cuda()
+    y_perm = make_dense((T * k, d), 1.0, seed=11, tag=1, device="cuda", dtype="bf16")
+    gate = torch.rand((T, k), generator=torch.Generator().manual_seed(11)).cuda()
+    p = moe.make_problem(T, d, E, k, 64, "bf16")
+    out = []
+    for nt in ("0", "1"):
+        os.environ["MOE_COMBINE_NT"] = nt
+        try:
+            y = torch.full((T, d), float("nan"), dtype=y_perm.dtype, device="cuda")
+            moe.moe_combine(p, y_perm, inv, gate, y)
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["MOE_COMBINE_NT"]
+        out.append(y)
+    assert torch.equal(out[0], out[1])
+    ref = oracle.combine(f64(y_perm), i64(inv).astype(np.int32), f64(gate))
+    assert rel_err(f64(out[1]), ref) <= 2 ** -8

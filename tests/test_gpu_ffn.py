@@ -192,3 +192,4 @@ def test_raster_groups_do_not_change_results(moe, blocks, split0):
         assert torch.equal(out[gm][1], out["0"][1]), gm
     ref = oracle_ffn("bf16", x, off.cpu(), W1, W2)
     assert rel_err(f64(out["8"][0]), ref) <= TOL_BF16
+
