@@ -24,11 +24,11 @@ TILES = ["auto", "256x256w8", "128x128", "256x128", "256x256", "256x256w8k32", "
 BASES = ["mixtral_coarse", "fine_grained", "skewed", "large_sparse"]
 
 
-def make_cases(n=24, seed=2024):
+def make_cases(n=24, seed=2024, experts=(1, 3, 8, 12, 16, 40, 64)):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
-        E = int(rng.choice([1, 3, 8, 12, 16, 40, 64]))
+        E = int(rng.choice(experts))
         k = int(rng.integers(1, min(E, 8) + 1)) if i % 7 else E if E <= 16 else 8
         cases.append(dict(
             base=BASES[i % len(BASES)],
@@ -45,7 +45,9 @@ def make_cases(n=24, seed=2024):
     return cases
 
 
-CASES = make_cases()
+# the first set, then wide expert counts: every padded router width (64,
+# 128, 192, 256 columns), including 129 .. 192 experts
+CASES = make_cases() + make_cases(n=8, seed=2025, experts=(72, 128, 136, 160, 192, 200, 256))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
