@@ -12,9 +12,10 @@ the kernels' own work and schedule, so the constants are a least-squares fit:
   route     a0 + (a1 + a2 * E64 / 64) * K steps of 64 in the busiest CU's
             chain of router blocks + a3 * thousands of partial logits a
             finalize wave adds per token (splits x E; small batches split
-            d_model) + a4 * M selections (a block scores 64 tokens against
-            the E64 experts padded to 64; most layers give every CU at most
-            one round of such blocks, so the serial chain, not HBM, sets the
+            d_model) + a4 * M selections (a block scores 64 tokens, or 32
+            where 64-token blocks would leave CUs idle, against the E64
+            experts padded to 64; most layers give every CU at most one
+            round of such blocks, so the serial chain, not HBM, sets the
             time)
   permute   b0 + b1 * [one-workgroup form, T <= 1024] + b2 * M selections
             (index arrays only: the token rows reach the first GEMM through
@@ -26,9 +27,10 @@ the kernels' own work and schedule, so the constants are a least-squares fit:
             tile (f0 comes out negative: the step count charges in full the
             first and last steps of a tile, which the pipeline overlaps with
             its neighbours)
-  combine   c0 + c1 * MB read and written + c2 * thousands of elements one
-            token's wave reads (k rows of d_model: the latency chain of small
-            batches)
+  combine   c0 + c1 * MB read and written (plain accesses) + c2 * MB read
+            and written (non-temporal, y_perm of 128 MB or more) + c3 *
+            thousands of elements one token's wave reads (k rows of d_model:
+            the latency chain of small batches)
 
 The terms replay the launcher's decisions: the router split, the permute
 form, the GEMM tile per problem, tiles per expert group dealt to 8 XCDs x
@@ -153,24 +155,34 @@ def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, floa
     return {"steps": steps * scale, "tiles": n_tiles * occ, "partial_mb": partial_mb, "stream_steps": 0.0}
 
 
+def route_rt(T: int, E: int) -> int:
+    """Tokens per router block: 32 where 64-token blocks would fill a quarter
+    to all of the CUs (too many to split over d_model) and E <= 128, else 64."""
+    b64 = math.ceil(T / 64)
+    return 32 if E <= 128 and b64 * 4 > CUS and b64 < CUS else 64
+
+
 def route_splits(T: int, d: int, E: int) -> int:
-    """The router's split over d_model: only when the 64-token blocks fill at
+    """The router's split over d_model: only when the router blocks fill at
     most a quarter of the CUs; about two blocks per CU, at least four K steps
     per split, at most 64 KB of partial logits per token."""
-    blocks = math.ceil(T / 64)
+    blocks = math.ceil(T / route_rt(T, E))
     if E % 8 or blocks * 4 > CUS:
         return 1
     ns = min(math.ceil(2 * CUS / blocks), (d // 64) // 4, 65536 // (E * 4))
     return max(ns, 1)
 
 
-def _route_blocks_per_cu(ep: int) -> int:
-    """Router blocks one CU holds at once: its LDS ring of 64 x 64 token
+def _route_blocks_per_cu(ep: int, rt: int = 64) -> int:
+    """Router blocks one CU holds at once: its LDS ring of rt x 64 token
     pieces and 64 x E64 weight pieces (4 stages up to 128 experts, else 3),
     or the float32 logits of the block when larger, out of 160 KB."""
     stages = 4 if ep <= 128 else 3
-    smem = max(stages * (64 * 64 * 2 + 64 * ep * 2), 64 * (ep + 1) * 4)
+    smem = max(stages * (rt * 64 * 2 + 64 * ep * 2), rt * (ep + 1) * 4)
     return max(1, 160 * 1024 // smem)
+
+
+COMBINE_STREAM_BYTES = 128 << 20  # y_perm size from which the combine streams (non-temporal accesses)
 
 
 def features(s: Sample) -> Dict[str, np.ndarray]:
@@ -180,9 +192,12 @@ def features(s: Sample) -> Dict[str, np.ndarray]:
     es = 2
     ep = math.ceil(E / 64) * 64
     ns = route_splits(T, d, E)
-    rounds = math.ceil(math.ceil(T / 64) * ns / (CUS * _route_blocks_per_cu(ep)))
+    rt = route_rt(T, E)
+    rounds = math.ceil(math.ceil(T / rt) * ns / (CUS * _route_blocks_per_cu(ep, rt)))
     chain = rounds * math.ceil(d / 64 / ns)
     small = 1.0 if T <= 1024 and k <= 8 else 0.0
+    mb = (R * d * es + T * d * es) / 1e6
+    stream = R * d * es >= COMBINE_STREAM_BYTES
     g1 = _gemm_terms(s.counts, d, de, E)
     g2 = _gemm_terms(s.counts, de, d, E)
     return {
@@ -190,7 +205,7 @@ def features(s: Sample) -> Dict[str, np.ndarray]:
         "permute": np.array([1.0, small, R / 1e6]),
         "ffn": np.array([2.0, g1["steps"] + g2["steps"], g1["tiles"] + g2["tiles"],
                          g1["partial_mb"] + g2["partial_mb"], g1["stream_steps"] + g2["stream_steps"]]),
-        "combine": np.array([1.0, (R * d * es + T * d * es) / 1e6, k * d / 1e3]),
+        "combine": np.array([1.0, 0.0 if stream else mb, mb if stream else 0.0, k * d / 1e3]),
     }
 
 
