@@ -17,9 +17,10 @@ the kernels' own work and schedule, so the constants are a least-squares fit:
             experts padded to 64; most layers give every CU at most one
             round of such blocks, so the serial chain, not HBM, sets the
             time)
-  permute   b0 + b1 * [one-workgroup form, T <= 1024] + b2 * M selections
-            (index arrays only: the token rows reach the first GEMM through
-            perm)
+  permute   b0 + b1 * [one-workgroup form, T <= 1024] + b2 * [separate
+            scan launch, more than 64 blocks of 256 tokens] + b3 * M
+            selections (index arrays only: the token rows reach the first
+            GEMM through perm)
   ffn       per grouped GEMM: f0 + f1 * K steps of 64 run by the busiest
             persistent block of a matrix-core tile + f2 * tiles that block
             runs + f3 * MB of split-tile partial sums written and read back
@@ -196,13 +197,14 @@ def features(s: Sample) -> Dict[str, np.ndarray]:
     rounds = math.ceil(math.ceil(T / rt) * ns / (CUS * _route_blocks_per_cu(ep, rt)))
     chain = rounds * math.ceil(d / 64 / ns)
     small = 1.0 if T <= 1024 and k <= 8 else 0.0
+    scan_launch = 1.0 if not small and math.ceil(T / 256) > 64 else 0.0
     mb = (R * d * es + T * d * es) / 1e6
     stream = R * d * es >= COMBINE_STREAM_BYTES
     g1 = _gemm_terms(s.counts, d, de, E)
     g2 = _gemm_terms(s.counts, de, d, E)
     return {
         "route": np.array([1.0, chain, chain * ep / 64, (ns * E / 1e3) if ns > 1 else 0.0, R / 1e6]),
-        "permute": np.array([1.0, small, R / 1e6]),
+        "permute": np.array([1.0, small, scan_launch, R / 1e6]),
         "ffn": np.array([2.0, g1["steps"] + g2["steps"], g1["tiles"] + g2["tiles"],
                          g1["partial_mb"] + g2["partial_mb"], g1["stream_steps"] + g2["stream_steps"]]),
         "combine": np.array([1.0, 0.0 if stream else mb, mb if stream else 0.0, k * d / 1e3]),

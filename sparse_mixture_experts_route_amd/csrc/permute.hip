@@ -11,7 +11,9 @@
 //           the order of the atomics); counts per (block, expert) = popcounts.
 //   scan    one workgroup: counts[e] over blocks, offsets[] as the exclusive
 //           prefix sum over experts, and the first row of every (block, expert),
-//           from the per-block counts staged in LDS.
+//           from the per-block counts staged in LDS. Up to kFusedScanBlocks
+//           blocks of tokens, each scatter block derives its own first rows
+//           from all the per-block counts instead (one launch fewer).
 //   scatter the row of selection (t, j) is the base of (block, e) plus the
 //           number of tokens before t in the block that selected e (popcount
 //           of the mask below t), so rows follow token order inside a group.
@@ -23,6 +25,8 @@
 // FIN form first completes a router split over d_model (partial logits summed
 // in split order, then the per-token selection), so that a decode-sized layer
 // goes from the router's partial logits to perm and inv in one launch.
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 #include "topk.h"
@@ -151,14 +155,58 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
 }
 
+// Up to this many blocks of tokens the scatter blocks derive their first rows
+// from the per-block counts themselves (each reads all nb x E counts), and the
+// separate scan launch is skipped.
+constexpr int kFusedScanBlocks = 64;
+
+// SCAN: `blockcounts` holds the per-block counts of hist_kernel (nb blocks);
+// every block sums them per expert (in total and over the blocks before it),
+// scans the totals over the experts, and block 0 writes counts and offsets.
+// Otherwise `blockcounts` is scan_kernel's first row of every (block, expert).
+template <bool SCAN>
 __global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
-                                                      const int32_t* __restrict__ blockbase,
+                                                      const int32_t* __restrict__ blockcounts, int64_t nb,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ uint32_t mask[256][kWords];
   __shared__ int32_t s_base[256];
   const int64_t t0 = (int64_t)blockIdx.x * kTB;
-  // this block's first row per expert (visible after build_mask's barriers)
-  if ((int)threadIdx.x < E) s_base[threadIdx.x] = blockbase[(int64_t)blockIdx.x * E + threadIdx.x];
+  const int e0 = threadIdx.x;  // kTB = 256 threads: one expert slot each
+  if constexpr (SCAN) {
+    int32_t tot = 0, before = 0;
+    if (e0 < E)
+      for (int64_t b0 = 0; b0 < nb; b0 += 16) {  // sixteen loads in flight
+        int32_t c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = b0 + u < nb ? blockcounts[(b0 + u) * E + e0] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          tot += c[u];
+          before += b0 + u < (int64_t)blockIdx.x ? c[u] : 0;
+        }
+      }
+    // inclusive Hillis-Steele scan of the totals over the 256 expert slots
+    s_base[e0] = tot;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int32_t v = e0 >= o ? s_base[e0 - o] : 0;
+      __syncthreads();
+      s_base[e0] += v;
+      __syncthreads();
+    }
+    const int32_t incl = s_base[e0];
+    if (blockIdx.x == 0 && e0 < E) {
+      counts[e0] = tot;
+      offsets[e0] = incl - tot;
+      if (e0 == E - 1) offsets[E] = incl;
+    }
+    __syncthreads();  // every slot has been read
+    s_base[e0] = incl - tot + before;
+  } else {
+    if (e0 < E) s_base[e0] = blockcounts[(int64_t)blockIdx.x * E + e0];
+  }
+  // this block's first row per expert is visible after build_mask's barriers
   build_mask(idx, T, k, E, mask, t0);
   const int64_t t = t0 + threadIdx.x;
   if (t >= T) return;
@@ -335,12 +383,21 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
   hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // MOE_PERMUTE_FUSED_SCAN=0|1 forces the choice (1 only within kFusedScanBlocks)
+  bool fused = nb <= kFusedScanBlocks;
+  const char* force = getenv("MOE_PERMUTE_FUSED_SCAN");
+  if (force && force[0]) fused = fused && atoi(force) != 0;
+  if (fused) {
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts,
+                       nb, counts, offsets, perm, inv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blockcounts, nb, p.E, counts, offsets,
                      blockbase);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockbase, perm,
-                     inv);
+  hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockbase, nb,
+                     counts, offsets, perm, inv);
   return hipGetLastError();
 }
 

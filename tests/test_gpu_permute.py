@@ -103,3 +103,25 @@ def test_permute_ignores_out_of_range_experts(moe):
     ph = i64(perm)
     for t, j in zip(*np.nonzero(valid)):
         assert ph[invh[t, j]] == t
+
+
+@pytest.mark.parametrize("T,E,k", [(1025, 256, 8), (5000, 64, 8), (16384, 8, 2), (9999, 200, 3)])
+def test_permute_scan_inside_scatter(moe, T, E, k):
+    """Up to 64 blocks of tokens the scatter blocks run the scan themselves
+    (no scan launch); forced back to the separate scan (MOE_PERMUTE_FUSED_SCAN=0)
+    every output is the same, bit for bit, and equals the oracle's."""
+    import os
+    announce(f"permute fused scan T={T} E={E} k={k}")
+    idx = make_routing_table(T, E, k, seed=21, hot=(1,)).cuda()
+    x = make_dense((T, 64), 1.0, seed=21, tag=1, device="cuda", dtype="bf16")
+    fused = run_permute(moe, T, 64, E, k, "bf16", idx, x)
+    os.environ["MOE_PERMUTE_FUSED_SCAN"] = "0"
+    try:
+        split = run_permute(moe, T, 64, E, k, "bf16", idx, x)
+    finally:
+        del os.environ["MOE_PERMUTE_FUSED_SCAN"]
+    for a, b in zip(fused, split):
+        assert torch.equal(a, b)
+    ref = oracle.permute(i64(idx).astype(np.int32), E)
+    for name, got in zip(("counts", "offsets", "perm", "inv"), fused[:4]):
+        assert np.array_equal(i64(got), ref[name]), name
