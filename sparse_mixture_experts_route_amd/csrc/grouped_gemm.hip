@@ -866,7 +866,15 @@ template <int BM, int BN>
 constexpr int fixup_sub() {
   return BM * BN / 4 / 256 >= 16 ? 16 : BM * BN / 4 / 256;
 }
-constexpr int kFixupRounds = 1;  // split tiles one fixup block may take in turn
+// split tiles one fixup block may take in turn: a grid for a quarter of the
+// most leftover tiles per XCD (MOE_FIXUP_ROUNDS=<n> overrides). Measured on
+// MI355X against one tile per block: the FFN phase equal within noise on
+// four workloads, ~1 % shorter at 8192 tokens x 64 experts
+constexpr int kFixupRounds = 4;
+int fixup_rounds() {
+  const char* fr = getenv("MOE_FIXUP_ROUNDS");
+  return fr && fr[0] ? max(1, atoi(fr)) : kFixupRounds;
+}
 
 template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2, bool FILL = false>
 hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
@@ -886,7 +894,7 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   const int gm = group_m();
   // fixup blocks: FS per split tile, each looping over up to kFixupRounds tiles
   constexpr int FS = fixup_sub<BM, BN>();
-  const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
+  const int fix_r = (max_rem + fixup_rounds() - 1) / fixup_rounds();
   const unsigned fix_grid = nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * FS) : 0u;
   constexpr int NT = WM * WN * 64;
   if (gelu && perm) {
@@ -928,7 +936,7 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
 // launches); no activation.
 hipError_t launch_split_fixup_256(const int32_t* offsets, const float* partials, uint16_t* C, int64_t R, int nk, int N,
                                   int E, int nb, int min_steps, int max_rem, hipStream_t s) {
-  const int fix_r = (max_rem + kFixupRounds - 1) / kFixupRounds;
+  const int fix_r = (max_rem + fixup_rounds() - 1) / fixup_rounds();
   if (nk < min_steps || max_rem <= 0) return hipSuccess;
   constexpr int FS = fixup_sub<256, 256>();
   hipLaunchKernelGGL((gemm_fixup_kernel<256, 256, 2, 4, FS, false>), dim3((unsigned)(8 * fix_r * FS)),

@@ -193,3 +193,29 @@ def test_raster_groups_do_not_change_results(moe, blocks, split0):
     ref = oracle_ffn("bf16", x, off.cpu(), W1, W2)
     assert rel_err(f64(out["8"][0]), ref) <= TOL_BF16
 
+
+
+@pytest.mark.parametrize("blocks", [64, 256])
+def test_fixup_rounds_do_not_change_results(moe, blocks):
+    """A fixup block may complete several split tiles in turn
+    (MOE_FIXUP_ROUNDS): each tile's partial sums are added in K order whichever
+    block takes it, so the outputs are equal bit for bit."""
+    R, d, de, E = 20000, 256, 192, 5
+    announce(f"ffn fixup rounds blocks={blocks}")
+    x = make_dense((R, d), 1.0, seed=14, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=14, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=14, tag=3, device="cuda")
+    off = make_group_offsets(E, R, seed=14).cuda()
+    out = {}
+    for rounds in ("1", "2", "4"):
+        env = {"MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_SPLIT_MIN_STEPS": "0", "MOE_FIXUP_ROUNDS": rounds,
+               "MOE_GEMM_TILE": "256x256w8"}
+        os.environ.update(env)
+        try:
+            out[rounds] = run_ffn(moe, R, d, de, E, "bf16", x, off, W1, W2)
+        finally:
+            for k in env:
+                del os.environ[k]
+    assert torch.equal(out["2"], out["1"]) and torch.equal(out["4"], out["1"])
+    ref = oracle_ffn("bf16", x, off.cpu(), W1, W2)
+    assert rel_err(f64(out["4"]), ref) <= TOL_BF16
