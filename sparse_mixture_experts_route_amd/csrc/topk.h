@@ -46,21 +46,53 @@ __device__ __forceinline__ void select_topk(const float* lg, int E, int k, int64
 }
 
 // Top-k (k <= kTopkFast) of the RT tokens of a block whose logits are in LDS
-// (row r at lg + r * ld): four threads per token, thread q of the group scans
-// experts q, q + 4, ... keeping the kTopkFast largest 64-bit keys (the keys of
-// select_topk: order-preserving logit bits above the inverted expert index,
-// all distinct) in a sorted register list; the four lists are merged over two
-// rounds of lane exchanges, so the result equals select_topk's selection.
-// Softmax maximum and sum are combined the same way (fixed order).
+// (row r at lg + r * ld): four threads per token; thread q of the group takes
+// experts q, q + 4, ... eight at a time. Keys are those of select_topk
+// (order-preserving logit bits above the inverted expert index, all
+// distinct). Each group of eight is sorted by a bitonic network and merged
+// into the thread's running top eight (the larger of top[i] and chunk[7 - i]
+// for every i is a bitonic sequence that holds the eight largest of both;
+// a bitonic merge sorts it), then the four threads' lists are merged the same
+// way over two rounds of lane exchanges. The keys being distinct, the result
+// is the unique top eight in descending order, as select_topk selects.
+// Softmax maximum and sum are combined over the four threads in fixed order.
 constexpr int kTopkFast = 8;
 
-__device__ __forceinline__ void insert_key(uint64_t (&top)[kTopkFast], uint64_t v) {
+__device__ __forceinline__ void cswap_desc(uint64_t& a, uint64_t& b) {  // a >= b afterwards
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// eight keys into descending order (bitonic sorting network, 24 compare-swaps)
+__device__ __forceinline__ void sort8_desc(uint64_t (&v)[kTopkFast]) {
 #pragma unroll
-  for (int j = 0; j < kTopkFast; ++j) {
-    const uint64_t hi = top[j] > v ? top[j] : v;
-    v = top[j] > v ? v : top[j];
-    top[j] = hi;
-  }
+  for (int kk = 2; kk <= kTopkFast; kk <<= 1)
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < kTopkFast; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          if ((i & kk) == 0)
+            cswap_desc(v[i], v[l]);
+          else
+            cswap_desc(v[l], v[i]);
+        }
+      }
+}
+
+// top (descending) becomes the eight largest of top and b (both descending)
+__device__ __forceinline__ void merge_top8(uint64_t (&top)[kTopkFast], const uint64_t (&b)[kTopkFast]) {
+#pragma unroll
+  for (int i = 0; i < kTopkFast; ++i) top[i] = top[i] > b[kTopkFast - 1 - i] ? top[i] : b[kTopkFast - 1 - i];
+#pragma unroll
+  for (int j = kTopkFast >> 1; j > 0; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < kTopkFast; ++i) {
+      const int l = i ^ j;
+      if (l > i) cswap_desc(top[i], top[l]);
+    }
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
@@ -78,10 +110,20 @@ __device__ __forceinline__ void select_topk_block(const float* lg, int ld, int64
 #pragma unroll
   for (int j = 0; j < kTopkFast; ++j) top[j] = 0;  // below every finite logit's key
   float m = -INFINITY;
-  for (int e = q; e < E; e += 4) {
-    const float l = row[e];
-    m = fmaxf(m, l);
-    insert_key(top, ((uint64_t)float_order_key(l) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e));
+  for (int e0 = q; e0 < E; e0 += 4 * kTopkFast) {
+    uint64_t c[kTopkFast];
+#pragma unroll
+    for (int j = 0; j < kTopkFast; ++j) {
+      const int e = e0 + 4 * j;
+      c[j] = 0;
+      if (e < E) {
+        const float l = row[e];
+        m = fmaxf(m, l);
+        c[j] = ((uint64_t)float_order_key(l) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+      }
+    }
+    sort8_desc(c);
+    merge_top8(top, c);
   }
   m = fmaxf(m, __shfl_xor(m, 1, kWave));
   m = fmaxf(m, __shfl_xor(m, 2, kWave));
@@ -94,8 +136,7 @@ __device__ __forceinline__ void select_topk_block(const float* lg, int ld, int64
     uint64_t other[kTopkFast];
 #pragma unroll
     for (int j = 0; j < kTopkFast; ++j) other[j] = shfl_xor_u64(top[j], o);
-#pragma unroll
-    for (int j = 0; j < kTopkFast; ++j) insert_key(top, other[j]);
+    merge_top8(top, other);
   }
   const int64_t t = t0 + r;
   if (q == 0 && t < T) {
