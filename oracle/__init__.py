@@ -26,6 +26,7 @@ from .moe_oracle import (  # noqa: F401
 from .moe_backward import (  # noqa: F401
     backward,
     backward64,
+    expert_backward,
     forward64_fixed,
     gelu_tanh_grad,
 )

@@ -53,6 +53,20 @@ def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
     return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * _C * (1.0 + 3.0 * _A * u * u)
 
 
+def expert_backward(X: np.ndarray, dYp: np.ndarray, w1e: np.ndarray, w2e: np.ndarray) -> Dict[str, np.ndarray]:
+    """One expert's forward (recomputed) and backward over its rows, float64.
+
+    X [rows, d] are the expert's input rows, dYp [rows, d] the gradients of its
+    gated outputs (g dy of each row's token): U = X W1_e, H = GELU_tanh(U),
+    Y = H W2_e, dH = dYp W2_e^T, dU = dH * GELU_tanh'(U), dX = dU W1_e^T,
+    dW2_e = H^T dYp (a sum over the rows), dW1_e = X^T dU."""
+    U = X @ w1e
+    H = gelu_tanh(U)
+    dH = dYp @ w2e.T
+    dU = dH * gelu_tanh_grad(U)
+    return {"U": U, "H": H, "Y": H @ w2e, "dU": dU, "dX": dU @ w1e.T, "dW1": X.T @ dU, "dW2": H.T @ dYp}
+
+
 def backward64(x64: np.ndarray, wr64: np.ndarray, W1: WeightSource, W2: WeightSource, k: int,
                dy64: np.ndarray, idx: np.ndarray, logits: np.ndarray) -> Dict[str, np.ndarray]:
     """The backward on float64 arrays, for a given selection `idx` [T, k] and the
@@ -89,16 +103,12 @@ def backward64(x64: np.ndarray, wr64: np.ndarray, W1: WeightSource, W2: WeightSo
             dW1[e] = np.zeros_like(w1e)
             dW2[e] = np.zeros_like(w2e)
             continue
-        X = xp[lo:hi]
-        U = X @ w1e
-        H = gelu_tanh(U)
-        Y[lo:hi] = H @ w2e
-        dH = dYp[lo:hi] @ w2e.T
-        dU = dH * gelu_tanh_grad(U)
-        dXp[lo:hi] = dU @ w1e.T
-        dW2[e] = H.T @ dYp[lo:hi]
-        dW1[e] = X.T @ dU
-        U_all[lo:hi], H_all[lo:hi], dU_all[lo:hi] = U, H, dU
+        g = expert_backward(xp[lo:hi], dYp[lo:hi], w1e, w2e)
+        Y[lo:hi] = g["Y"]
+        dXp[lo:hi] = g["dX"]
+        dW2[e] = g["dW2"]
+        dW1[e] = g["dW1"]
+        U_all[lo:hi], H_all[lo:hi], dU_all[lo:hi] = g["U"], g["H"], g["dU"]
 
     # combine backward: gate gradients
     dG = np.zeros((T, k), dtype=np.float64)

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import TOL_BF16, TOL_F32, announce, f64, i64, needs_gpu, rel_err
+from gpu_helpers import TOL_BF16, TOL_F32, announce, check_routing_e2e, check_routing_exact, f64, needs_gpu, rel_err
 from harness import host_array, make_inputs, scaled_config
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -75,11 +75,9 @@ def test_random_shape(moe, case):
     assert torch.equal(y, st["y"]), "moe_forward and the stage calls must agree bitwise"
     h = {key: host_array(v) for key, v in inp.items()}
     ref = oracle.forward(h["x"], h["w_router"], h["router_bias"], h["W1"], h["W2"], cfg.k, cfg.dtype)
-    idx = i64(st["idx"])
-    tie = ref["near_tie"]
-    same = np.array([set(idx[t]) == set(ref["idx"][t]) for t in range(cfg.T)])
-    assert not (~same & ~tie).any(), "routing differs outside near-ties"
-    keep = ~tie
+    logits, idx, _ = check_routing_exact(cfg, st)
+    x64, wr64 = oracle.decode(h["x"], cfg.dtype), oracle.decode(h["w_router"], cfg.dtype)
+    keep = check_routing_e2e(cfg, logits, idx, f64(st["gate"]), x64, wr64, h["router_bias"], ref)
     if keep.any():
         err = rel_err(f64(y)[keep], ref["y"][keep])
         assert err <= (TOL_F32 if cfg.dtype == "f32" else TOL_BF16), err
