@@ -181,6 +181,114 @@ def train_step(args, cfg, moe, inp, dev):
     }
 
 
+PHASE_NAMES = ("route", "permute", "ffn", "combine")
+
+
+def settle(step, seconds):
+    """Untimed steps for at least `seconds` of wall time; returns the time spent."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return dt
+
+
+def headline(step, warmup, steps, stream):
+    """`warmup` untimed steps, then exactly `steps` steps bracketed by HIP
+    events on the stream the kernels run on (and synchronisations)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return {"ms": ev[0].elapsed_time(ev[-1]) / steps, "median": per[len(per) // 2], "min": per[0], "wall": wall}
+
+
+def phase_times(moe, cfg, layer, x, wr, b, W1, W2, warmup, steps, stream, dev):
+    """Per-phase times of the stage entry points moe_forward runs (route with
+    a workspace, permute of the indices, grouped FFN reading x through perm
+    for bf16 layers under 2 GiB of x; else the copy path), with HIP events
+    between the phases; mean over `steps` steps after `warmup` untimed ones."""
+    import torch
+    p = layer.problem
+    bufs = layer.stages(x, wr, W1, W2, b, logits=False)  # allocates the stage outputs once
+    ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
+    gather = cfg.dtype == "bf16" and cfg.T * cfg.d_model * 2 < 2 ** 31 - 1
+
+    def stage_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_route_ws(p, x, wr, b, None, bufs["idx"], bufs["gate"], ws_r)
+        if ev is not None:
+            ev[1].record(stream)
+        if gather:
+            moe.moe_permute_index(p, bufs["idx"], bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"], ws_p)
+        else:
+            moe.moe_permute(p, bufs["idx"], x, bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"],
+                            bufs["x_perm"], ws_p)
+        if ev is not None:
+            ev[2].record(stream)
+        if gather:
+            moe.moe_grouped_ffn_gather(p, x, bufs["perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
+        else:
+            moe.moe_grouped_ffn(p, bufs["x_perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.moe_combine(p, bufs["y_perm"], bufs["inv"], bufs["gate"], bufs["y"])
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        stage_step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for s in range(steps):
+        stage_step(events[s])
+    torch.cuda.synchronize()
+    ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, n in enumerate(PHASE_NAMES)}
+    return {"ms": ms, "gather": gather, "y": bufs["y"], "used_experts": int((bufs["counts"] > 0).sum().item())}
+
+
+def extra_config(moe, cfg, args, stream, dev):
+    """Whole-layer tokens/s and the grouped-FFN phase's TFLOP/s of another
+    workload, measured like the headline one (settle, warm-up, timed steps,
+    then the per-phase region)."""
+    import torch
+    from harness import make_inputs
+    inp = make_inputs(cfg, seed=args.seed, device=dev)
+    x, wr, b, W1, W2 = inp["x"], inp["w_router"], inp["router_bias"], inp["W1"], inp["W2"]
+    layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, x.dtype, device=dev)
+    steps = args.steps if cfg.ffn_flops() < 2e12 else max(5, args.steps // 2)
+    settle(lambda: layer(x, wr, W1, W2, b), args.settle_seconds / 2)
+    head = headline(lambda: layer(x, wr, W1, W2, b), args.warmup, steps, stream)
+    ph = phase_times(moe, cfg, layer, x, wr, b, W1, W2, args.warmup, steps, stream, dev)
+    ffn_tflops = cfg.ffn_flops() / (ph["ms"]["ffn"] * 1e-3) / 1e12
+    out = {"config": cfg.describe(), "steps": steps, "ms_per_step": round(head["ms"], 4),
+           "tokens_per_s": round(cfg.T / (head["ms"] * 1e-3), 1),
+           "phases_ms": {n: round(v, 4) for n, v in ph["ms"].items()},
+           "ffn_tflops": round(ffn_tflops, 2),
+           "ffn_frac_of_bf16_peak": round(ffn_tflops / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
+           "phase_sum_over_step": round(sum(ph["ms"].values()) / head["ms"], 4)}
+    del inp, x, wr, b, W1, W2, layer, ph
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +306,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle pass until this much wall time has elapsed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="untimed whole-layer steps for this long before the warm-up (clocks reach steady state)")
+    ap.add_argument("--extra-configs", default="fine_grained,large_sparse",
+                    help="other workloads whose tokens/s and FFN TFLOP/s are added to the line ('' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -236,71 +348,23 @@ def main():
         print(json.dumps(train_step(args, cfg, moe, inp, dev)), flush=True)
         return
 
-    # ---- per-phase region: the same work through the four stage entry points,
-    # with HIP events between phases on the stream the kernels run on. It runs
-    # first: the GPU's clocks take tens of milliseconds of load to settle, and
-    # the headline region below should measure the steady state
-    p = layer.problem
-    R = cfg.T * cfg.k
-    bufs = layer.stages(x, wr, W1, W2, b, logits=False)  # allocates the stage outputs once
-    ws_p = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_PERMUTE), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device=dev)
-    ws_r = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_ROUTE), dtype=torch.uint8, device=dev)
-    names = ["route", "permute", "ffn", "combine"]
-    # the stage calls moe_forward itself makes: bf16 folds the dispatch into the first GEMM
-    gather = cfg.dtype == "bf16" and cfg.T * cfg.d_model * 2 < 2 ** 31 - 1
-
-    def stage_step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        moe.moe_route_ws(p, x, wr, b, None, bufs["idx"], bufs["gate"], ws_r)
-        if ev is not None:
-            ev[1].record(stream)
-        if gather:
-            moe.moe_permute_index(p, bufs["idx"], bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"], ws_p)
-        else:
-            moe.moe_permute(p, bufs["idx"], x, bufs["counts"], bufs["offsets"], bufs["perm"], bufs["inv"],
-                            bufs["x_perm"], ws_p)
-        if ev is not None:
-            ev[2].record(stream)
-        if gather:
-            moe.moe_grouped_ffn_gather(p, x, bufs["perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
-        else:
-            moe.moe_grouped_ffn(p, bufs["x_perm"], bufs["offsets"], W1, W2, bufs["y_perm"], ws_f)
-        if ev is not None:
-            ev[3].record(stream)
-        moe.moe_combine(p, bufs["y_perm"], bufs["inv"], bufs["gate"], bufs["y"])
-        if ev is not None:
-            ev[4].record(stream)
-
-    for _ in range(args.warmup):
-        stage_step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        stage_step(events[s])
-    torch.cuda.synchronize()
-    phase_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, n in enumerate(names)}
-
-    # ---- timed region: whole-layer steps through moe_forward (the headline)
-    for _ in range(args.warmup):
-        layer(x, wr, W1, W2, b)
-    torch.cuda.synchronize()
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    wall0 = time.perf_counter()
-    step_ev[0].record(stream)
-    for i in range(args.steps):
-        layer(x, wr, W1, W2, b)
-        step_ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = step_ev[0].elapsed_time(step_ev[-1]) / args.steps
-    per_step = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
-
-    assert torch.equal(bufs["y"], layer.y), "stage path and moe_forward disagree"
+    # ---- settle: the GPU's clocks take a second or so of matrix-core load to
+    # reach their steady state; this untimed load comes before the warm-up
+    # steps, so the warm-up and both timed regions below run at steady clocks
+    settle_s = settle(lambda: layer(x, wr, W1, W2, b), args.settle_seconds)
+    head = headline(lambda: layer(x, wr, W1, W2, b), args.warmup, args.steps, stream)
+    # ---- per-phase region, after the headline: the same work through the
+    # stage entry points moe_forward itself calls, with HIP events between
+    # the phases on the stream the kernels run on
+    ph = phase_times(moe, cfg, layer, x, wr, b, W1, W2, args.warmup, args.steps, stream, dev)
+    assert torch.equal(ph["y"], layer.y), "stage path and moe_forward disagree"
+    phase_ms = ph["ms"]
+    gather = ph["gather"]
 
     flops = cfg.ffn_flops()
-    used = int((bufs["counts"] > 0).sum().item())
+    used = ph["used_experts"]
     bytes_ = algorithmic_bytes(cfg, gather, used)
+    ms_step = head["ms"]
     t_ffn = phase_ms["ffn"] * 1e-3
     ffn_tflops = flops / t_ffn / 1e12
     # the FFN phase is bound by the matrix cores when its flops per algorithmic
@@ -329,8 +393,15 @@ def main():
     phases = {n: {"ms": round(phase_ms[n], 4),
                   "GB/s": round(bytes_[n] / (phase_ms[n] * 1e-3) / 1e9, 1),
                   "hbm_frac": round(bytes_[n] / (phase_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-              for n in names}
+              for n in PHASE_NAMES}
     phases["ffn"]["TFLOP/s"] = round(ffn_tflops, 2)
+    phase_sum = sum(phase_ms.values())
+    # the phases run the same kernels as a moe_forward step, with events between
+    # them: their sum should not exceed the step by more than the events' cost
+    consistent = phase_sum <= 1.05 * ms_step
+    if not consistent:
+        print(f"bench.py: phase sum {phase_sum:.4f} ms exceeds 1.05 x the step ({ms_step:.4f} ms)",
+              file=sys.stderr)
 
     result = {
         "metric": METRIC,
@@ -340,8 +411,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
-        "ms_per_step_min": round(per_step[0], 4),
+        "ms_per_step_median": round(head["median"], 4),
+        "ms_per_step_min": round(head["min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -351,10 +422,19 @@ def main():
         "ffn_tflops": round(ffn_tflops, 2),
         "ffn_frac_of_bf16_peak": round(ffn_tflops / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
         "phases": phases,
+        "phase_sum_over_step": round(phase_sum / ms_step, 4),
+        "phases_consistent": consistent,
         "roofline": roofline,
-        "wall_s_timed_region": round(wall, 4),
+        "settle_s": round(settle_s, 2),
+        "wall_s_timed_region": round(head["wall"], 4),
         "gpu": torch.cuda.get_device_name(dev),
     }
+    del layer, ph
+    if args.extra_configs and not (args.tokens or args.k):
+        extra = {}
+        for name in [c for c in args.extra_configs.split(",") if c and c != cfg.name]:
+            extra[name] = extra_config(moe, CONFIGS[name], args, stream, dev)
+        result["extra_configs"] = extra
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_seconds)
     print(json.dumps(result), flush=True)
