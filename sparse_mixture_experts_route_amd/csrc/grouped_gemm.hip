@@ -50,6 +50,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "gemm_lanes.h"
 #include "internal.h"
 #include "lds_dma.h"
 #include "tiles.h"
@@ -211,13 +212,13 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     tile_coords(local, mt, n_tiles, gm, n_tile, m_idx);
     tl.row0 = (int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e]) + (int64_t)m_idx * BM;
     tl.row_end = min((int64_t)__builtin_amdgcn_readfirstlane(offsets[tl.e + 1]), R);
-    tl.n0 = n_tile * BN;
+    tl.n0 = lanes::tile_n0(n_tile, n_tiles, N, BN);
     // A: rows row0.. of the group; rows past the group's end fall outside the
     // descriptor's range and read as zero. B: the expert's [K, N] slab.
     if constexpr (GATHER)
       tl.rsA = buffer_rsrc(A, (uint32_t)(a_rows * K * 2));
     else
-      tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)((tl.row_end - tl.row0) * K * 2));
+      tl.rsA = buffer_rsrc(A + tl.row0 * K, (uint32_t)(min(tl.row_end - tl.row0, (int64_t)BM) * K * 2));
     tl.rsB = buffer_rsrc(B + (int64_t)tl.e * K * N, (uint32_t)((int64_t)K * N * 2));
     tl.kb = 0;
     tl.kn = nk;
@@ -239,11 +240,10 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   int a_row[A_LD], a_c8[A_LD];  // row of the tile and first element of the lane's A piece
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int p = (wave * A_LD + i) * 64 + lane;  // LDS slot
-    const int row = p / A_CH, c = (p % A_CH) ^ ((row / A_RPP) & (A_CH - 1));
-    a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
-    a_row[i] = row;
-    a_c8[i] = c * 8;
+    const lanes::Piece pc = lanes::a_piece<BK>((wave * A_LD + i) * 64 + lane);  // LDS slot -> piece
+    a_off[i] = lanes::a_lane_off(pc, K);
+    a_row[i] = pc.row;
+    a_c8[i] = pc.c * 8;
   }
   // GATHER: the token rows of a tile's A pieces (-1 past the group's end), and
   // the byte offsets made from them; padding rows point past the range (read
@@ -259,16 +259,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     if constexpr (GATHER) {
 #pragma unroll
       for (int i = 0; i < A_LD; ++i)
-        t_.ga[i] = pv[i] >= 0 ? (uint32_t)(((int64_t)pv[i] * K + a_c8[i]) * 2) : 0xFFFFFFF0u;
+        t_.ga[i] = pv[i] >= 0 ? (uint32_t)(((int64_t)pv[i] * K + a_c8[i]) * 2) : lanes::kOutOfRange;
     }
   };
   uint32_t b_off0[B_LD];  // for n0 = 0
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int p = (wave * B_LD + i) * 64 + lane;
-    const int k = p / B_SLOTS, c = (p % B_SLOTS) ^ (4 * (k & 3));
-    b_off0[i] = (uint32_t)(k * N + c * 8) * 2u;
-  }
+  for (int i = 0; i < B_LD; ++i) b_off0[i] = lanes::b_lane_off(lanes::b_piece<BN>((wave * B_LD + i) * 64 + lane), N);
 
   // load `i` (0 .. NL-1) of stage kt into ring buffer buf
   auto issue_one = [&](const Tile& tl, int kt, int buf, int i) {
@@ -276,7 +272,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     if (i < A_LD)
       buffer_load_lds16(tl.rsA, GATHER ? tl.ga[i] : a_off[i], (uint32_t)kt * BK * 2, st + (wave * A_LD + i) * 1024);
     else
-      buffer_load_lds16(tl.rsB, b_off0[i - A_LD] + (uint32_t)tl.n0 * 2, (uint32_t)kt * BK * N * 2,
+      buffer_load_lds16(tl.rsB, b_off0[i - A_LD] + (uint32_t)tl.n0 * 2u, (uint32_t)kt * BK * N * 2,
                         st + A_STAGE + (wave * B_LD + i - A_LD) * 1024);
   };
 
@@ -557,7 +553,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
       constexpr int P_ITERS = EP_ITERS / PASSES;             // 16-byte stores per lane per pass
       lds_char* const ep = lds + (EARLY ? STAGE + wave * (EP_WAVE / 2) : wave * EP_WAVE);
       const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(C + tl.row0 * N), (short)0, (int)((tl.row_end - tl.row0) * N * 2), kBufferFlags);
+          (void*)(C + tl.row0 * N), (short)0, (int)(min(tl.row_end - tl.row0, (int64_t)BM) * N * 2), kBufferFlags);
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
@@ -597,7 +593,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
           for (int u = 0; u < EP_G; ++u) {
             const int idx = (it0 + u) * kWave + lane, row = idx / EP_CH, ch = idx % EP_CH;
             const int n = tl.n0 + wn0 + ch * 8;
-            const int off = n < N ? ((wm0 + pass * (WTM / PASSES) + row) * N + n) * 2 : 0x7FFFFFF0;
+            const int off = lanes::c_store_off(wm0 + pass * (WTM / PASSES) + row, n, N);
             __builtin_amdgcn_raw_buffer_store_b128(v[u], rsC, off, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -698,7 +694,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
     tile_coords(local, mt, n_tiles, gm, n_tile, m_idx);
     const int64_t row0 = (int64_t)offsets[e] + (int64_t)m_idx * BM;
     const int64_t row_end = min((int64_t)offsets[e + 1], R);
-    const int n0 = n_tile * BN;
+    const int n0 = lanes::tile_n0(n_tile, n_tiles, N, BN);
 
     f32x4 acc[PER];
 #pragma unroll
@@ -730,7 +726,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
       const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
       const int64_t grow = row0 + row;
       const int n = n0 + col;
-      if (grow >= row_end || n >= N) continue;
+      if (grow >= row_end || n < 0 || n >= N) continue;
       float v[4];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];

@@ -45,6 +45,7 @@
 #include <stdlib.h>
 
 #include "common.h"
+#include "gemm_lanes.h"
 #include "internal.h"
 #include "lds_dma.h"
 #include "tiles.h"
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
         rsA = buffer_rsrc(args.A + row0 * args.lda, (uint32_t)((row_end - row0) * args.lda * 2));
       rsB = buffer_rsrc(args.B + row0 * args.ldb, (uint32_t)((row_end - row0) * args.ldb * 2));
     } else {
-      rsA = buffer_rsrc(args.A + row0 * args.lda, (uint32_t)((row_end - row0) * args.lda * 2));
+      rsA = buffer_rsrc(args.A + row0 * args.lda, (uint32_t)(min(row_end - row0, (int64_t)kBM) * args.lda * 2));
       rsB = buffer_rsrc(args.B + (int64_t)e * args.b_estride, (uint32_t)((int64_t)args.N * args.ldb * 2));
     }
     // per-lane offsets that do not depend on the K step
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       if constexpr (B_MN)
         b_off[i] = (uint32_t)(mn_k[i] * args.ldb + n0 + mn_c8[i]) * 2u;
       else  // weight rows n0 + kc_row ([N, K] storage), columns past N point past the range
-        b_off[i] = n0 + kc_row[i] < args.N ? (uint32_t)((n0 + kc_row[i]) * args.ldb + kc_c8[i]) * 2u : 0xFFFFFFF0u;
+        b_off[i] = n0 + kc_row[i] < args.N ? (uint32_t)((n0 + kc_row[i]) * args.ldb + kc_c8[i]) * 2u : lanes::kOutOfRange;
     }
     // gathered A rows: the token of each k row of the next stage, looked up one stage ahead
     int gat[kLd];
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bwd_kernel(BwdArgs args) {
       for (int i = 0; i < kLd; ++i) {
         const uint32_t la = st + (wave * kLd + i) * 1024;
         if constexpr (GATHER_A) {
-          const uint32_t off = gat[i] >= 0 ? (uint32_t)(((int64_t)gat[i] * args.lda + m0 + mn_c8[i]) * 2) : 0xFFFFFFF0u;
+          const uint32_t off = gat[i] >= 0 ? (uint32_t)(((int64_t)gat[i] * args.lda + m0 + mn_c8[i]) * 2) : lanes::kOutOfRange;
           buffer_load_lds16(rsA, off, 0u, la);
         } else if constexpr (A_MN) {
           buffer_load_lds16(rsA, a_off[i], (uint32_t)kt * kBK * args.lda * 2u, la);

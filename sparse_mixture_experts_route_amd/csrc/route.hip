@@ -25,6 +25,7 @@
 //     (order-preserving logit key in the upper half, inverted expert index in
 //     the lower half, so equal logits favour the lower index).
 #include "common.h"
+#include "gemm_lanes.h"
 #include "internal.h"
 #include "lds_dma.h"
 #include "topk.h"
@@ -101,9 +102,8 @@ __global__ __launch_bounds__(RT * 4) void route_mfma_kernel(const bf16_bits* __r
   const i32x4 rsB = buffer_rsrc(wr, (uint32_t)(d * E_real * 2));
 
   // per-lane DMA offsets: x piece (row, chunk), w piece (k, chunk); chunks of
-  // padded experts (>= E_real) point past the range and load zeros (were the
-  // scalar K offset to wrap them back into range, they would read other w
-  // elements into columns that are never used)
+  // padded experts (>= E_real) point past the range and load zeros, also with
+  // the scalar K offset added (no 32-bit wrap: see lanes::kOutOfRange)
   uint32_t a_off[A_LD], b_off[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(RT * 4) void route_mfma_kernel(const bf16_bits* __r
   for (int i = 0; i < B_LD; ++i) {
     const int p = (wave * B_LD + i) * kWave + lane;
     const int kk = p / B_SLOTS, c = (p % B_SLOTS) ^ (BSW * (kk & 3));
-    b_off[i] = c * 8 < E_real ? (uint32_t)(kk * E_real + c * 8) * 2u : 0xFFFFFFF0u;
+    b_off[i] = c * 8 < E_real ? (uint32_t)(kk * E_real + c * 8) * 2u : lanes::kOutOfRange;
   }
   auto issue_one = [&](int kt, int buf, int i) {
     const uint32_t st = lds_base + buf * STAGE;
