@@ -143,6 +143,22 @@ moe_status_t moe_permute_index(const moe_problem_t* p, const int32_t* topk_idx, 
                                int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* moe_permute_index for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): the same counts, offsets, perm and inv, bit for bit, with no
+ * workspace argument. The counting sort's per-block counts and first rows
+ * live in a static device array of the library (2 * MOE_NOALLOC_PERMUTE_SLOTS
+ * int32, 2 MiB, held on each GPU the library runs on until the process ends),
+ * so ceil(T / 256) * E must not exceed MOE_NOALLOC_PERMUTE_SLOTS (e.g. T up
+ * to 262144 tokens with 256 experts): larger problems return
+ * MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued. Every call on a
+ * GPU uses that GPU's one array: calls that overlap on one GPU (different
+ * streams, or threads) race and must be ordered by the caller. The array is
+ * fully rewritten by each call before it is read. */
+#define MOE_NOALLOC_PERMUTE_SLOTS 262144
+moe_status_t moe_permute_index_noalloc(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
+
 /* moe_grouped_ffn with the dispatch folded into the first GEMM: row r of the
  * permuted input is read as x[perm[r]] (the same values moe_permute's x_perm
  * holds), so no permuted copy of x is written or read; y_perm is the same,

@@ -45,6 +45,7 @@ def _load():
         "moe_permute": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute_index": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_permute_index_noalloc": [P, vp, vp, vp, vp, vp, vp],
         "moe_grouped_ffn_gather": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [P, vp, vp, vp, vp, vp],
         "moe_forward": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -137,6 +138,11 @@ def moe_permute_index(p: Problem, topk_idx, counts, offsets, perm, inv, ws, stre
     _check(_lib.moe_permute_index(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
                                   _ptr(inv), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_permute_index")
+
+
+def moe_permute_index_noalloc(p: Problem, topk_idx, counts, offsets, perm, inv, stream=None):
+    _check(_lib.moe_permute_index_noalloc(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                                          _ptr(inv), _stream(stream)), "moe_permute_index_noalloc")
 
 
 def moe_grouped_ffn_gather(p: Problem, x, perm, offsets, W1, W2, y_perm, ws, stream=None):

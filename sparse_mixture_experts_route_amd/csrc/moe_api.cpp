@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -446,6 +447,57 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   if (e == hipSuccess && (dbias || load_frac || mean_prob))
     e = moe::launch_bwd_stats(*p, w.prob, w.dlogit, w.counts, w.stat_part, load_frac, mean_prob, dbias, s);
   return hip_status(e);
+}
+
+// ---- the index permute without a workspace argument
+
+namespace {
+
+// Per-block counts and per-block first rows of the counting sort (kNoAllocSlots
+// int32 each) in device memory of the library itself: each GPU the library
+// runs on holds its own copy until the process ends. In host code `scratch`
+// names a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocSlots = MOE_NOALLOC_PERMUTE_SLOTS;
+static __device__ __align__(256) int32_t scratch[2 * kNoAllocSlots];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices];  // device address of `scratch` per device, looked up once
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current).
+hipError_t device_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch[dev] = (int32_t*)ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+MOE_API moe_status_t moe_permute_index_noalloc(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                                               int32_t* offsets, int32_t* perm, int32_t* inv, void* stream) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) || !aligned16(inv))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (moe::permute_blocks(p->T) * (int64_t)p->E > kNoAllocSlots) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  int32_t* base = nullptr;
+  if (device_scratch(&base) != hipSuccess) return MOE_ERR_HIP;
+  // the kernels overwrite both arrays before reading them: nothing to clear
+  return hip_status(moe::launch_permute_index(*p, topk_idx, counts, offsets, perm, inv, base, base + kNoAllocSlots,
+                                              (hipStream_t)stream));
 }
 
 MOE_API const char* moe_status_str(int32_t status) {

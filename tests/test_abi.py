@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "moe_workspace_size", "moe_route", "moe_route_ws", "moe_permute", "moe_permute_index", "moe_grouped_ffn",
+        "moe_workspace_size", "moe_route", "moe_route_ws", "moe_permute", "moe_permute_index",
+        "moe_permute_index_noalloc", "moe_grouped_ffn",
         "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_forward_train", "moe_backward",
         "moe_status_str"])
 
@@ -162,3 +163,16 @@ def test_route_ws_rejects_before_launch_and_sizes_its_partials(moe, lib):
     assert moe.moe_workspace_size(big, moe.MOE_STAGE_ROUTE) <= 256
     f32 = P(moe, T=8, d=2048, E=8, k=2, de=256, dtype=0)
     assert moe.moe_workspace_size(f32, moe.MOE_STAGE_ROUTE) <= 256
+
+
+def test_permute_index_noalloc_rejects_before_launch(moe, lib):
+    """Bad pointers, and problems whose per-block arrays exceed the static
+    scratch (ceil(T / 256) * E > MOE_NOALLOC_PERMUTE_SLOTS), fail on the host."""
+    s = None
+    p = P(moe, T=5000, d=128, E=64, k=8, de=256)
+    assert lib.moe_permute_index_noalloc(ctypes.byref(p), None, A, A, A, A, s) == INVALID
+    assert lib.moe_permute_index_noalloc(ctypes.byref(p), A, A, A, MIS, A, s) == INVALID
+    slots = int(re.search(r"#define MOE_NOALLOC_PERMUTE_SLOTS (\d+)", open(HEADER).read()).group(1))
+    T_max = slots // 256 * 256  # ceil(T / 256) * 256 experts == slots
+    big = P(moe, T=T_max + 1, d=128, E=256, k=2, de=256)
+    assert lib.moe_permute_index_noalloc(ctypes.byref(big), A, A, A, A, A, s) == WS_SMALL
