@@ -107,11 +107,87 @@ __device__ __forceinline__ void find_tile(const int32_t* __restrict__ offsets, i
   __syncthreads();
 }
 
+// The partial-sum slots of leftover tile r of XCD x's tile range, in block
+// (= K) order, as split_k cuts the rem * nk (tile, K step) units over the XCD's
+// nb blocks; a block's slot for its leftover tile i is 2 * (block index) + i.
+// Wave 0 only (lane jj checks block jj, nb <= 64). Returns the number of slots
+// (written to s_slots), or -1 when one block ran the whole tile and stored it.
+__device__ __forceinline__ int split_tile_slots(int r, int rem, int nb, int nk, int x, int* s_slots) {
+  const int64_t W = (int64_t)rem * nk, u0 = (int64_t)r * nk, u1 = u0 + nk;
+  const int jj = threadIdx.x;
+  bool touch = false, whole = false;
+  int slot = 0;
+  if (jj < nb) {
+    const int64_t s0 = W * jj / nb, s1 = W * (jj + 1) / nb;
+    touch = s1 > s0 && s0 < u1 && s1 > u0;
+    whole = touch && s0 <= u0 && s1 >= u1;
+    slot = (jj * 8 + x) * 2 + (r - (int)(s0 / nk));
+  }
+  const uint64_t tm = __ballot(touch), wm = __ballot(whole);  // every lane of the wave votes
+  if (touch) s_slots[__popcll(tm & ((1ull << jj) - 1ull))] = slot;
+  return wm ? -1 : __popcll(tm);
+}
+
+// Completion of a split tile from its partial-sum slots: the float32x4
+// entries ebase + u * STRIDE (u < PER) of the slot layout the GEMM kernel
+// writes (thread-major per MFMA register group of its WM x WN waves) are
+// summed over slots[0 .. ns) in that order (deterministic: the same bits
+// whichever block completes the tile), then activation, bf16 rounding and
+// stores of the rows before row_end and the columns inside [0, N). G slots'
+// loads are in flight together.
+template <int BM, int BN, int WM, int WN, int PER, int STRIDE, int G, bool GELU>
+__device__ __forceinline__ void complete_split_entries(const float* __restrict__ partials, const int* slots, int ns,
+                                                       int ebase, bf16_bits* __restrict__ C, int64_t row0,
+                                                       int64_t row_end, int n0, int N) {
+  constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
+  f32x4 acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int si = 0; si < ns; si += G) {
+    f32x4 v[G][PER];
+#pragma unroll
+    for (int q4 = 0; q4 < G; ++q4) {
+      const int sl = si + q4 < ns ? slots[si + q4] : -1;
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        v[q4][u] = sl >= 0 ? ((const f32x4*)(partials + (int64_t)sl * (BM * BN)))[ebase + u * STRIDE]
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < G; ++q4)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
+    const int en = ebase + u * STRIDE, grp = en / (NW * kWave), tt = en % (NW * kWave);
+    const int mi = grp / (TN * 4), ni = (grp / 4) % TN, gq = grp % 4;
+    const int wave = tt / kWave, lane = tt % kWave;
+    const int row = (wave / WN) * WTM + mi * 32 + (lane & 31);
+    const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
+    const int64_t grow = row0 + row;
+    const int n = n0 + col;
+    if (grow >= row_end || n < 0 || n >= N) continue;
+    float v[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];
+    u32x2 o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    *(u32x2*)(C + grow * N + n) = o;
+  }
+}
+
 // Block tile BM x BN over K steps of BK, a ring of S LDS stages, OCC blocks per
 // CU, WM x WN waves (each owns a (BM/WM) x (BN/WN) piece of the tile).
 // GATHER: row r of A is row perm[r] of a [a_rows, K] matrix (the first expert
 // GEMM reading the tokens straight from x, with no permuted copy).
-template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU, bool GATHER = false>
+// INK: split tiles are completed inside the launch: the last of a tile's
+// blocks to store its partial sums (a counter per leftover tile in
+// `counters`, zero at the start, reset by that block) adds the slots in K
+// order and stores the tile, as gemm_fixup_kernel would; no block waits.
+template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU, bool GATHER = false, bool INK = false>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16_bits* __restrict__ A,
                                                                       const int32_t* __restrict__ offsets,
                                                                       const bf16_bits* __restrict__ B,
@@ -120,7 +196,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
                                                                       int N, int E, int n_tiles, int min_steps,
                                                                       int max_rem,
                                                                       const int32_t* __restrict__ perm,
-                                                                      int64_t a_rows, int gm) {
+                                                                      int64_t a_rows, int gm,
+                                                                      int32_t* __restrict__ counters) {
   constexpr int NW = WM * WN;                  // waves
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -149,6 +226,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   __shared__ int s_tstart[257];
   __shared__ int s_mtiles[256];
+  __shared__ int s_slots[INK ? 64 : 1];  // INK: slots of the split tile being completed
+  __shared__ int s_done;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -195,6 +274,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     int64_t row0, row_end;
     i32x4 rsA, rsB;
     int kb, kn, slot;  // first K step, K steps, partial-sum slot (-1: the item completes the tile)
+    int r;             // leftover tile index in the XCD's range (split items)
     uint32_t ga[GATHER ? A_LD : 1];  // GATHER: per-lane byte offsets of the A loads in A
   };
   auto locate = [&](int t) {
@@ -223,6 +303,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     tl.kb = 0;
     tl.kn = nk;
     tl.slot = -1;
+    tl.r = -1;
     return tl;
   };
   auto make_item = [&](int i) {
@@ -233,6 +314,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
     tl.kb = (int)(a0 - (int64_t)r * nk);
     tl.kn = (int)(b0 - a0);
     tl.slot = tl.kn == nk ? -1 : (int)blockIdx.x * 2 + (i - sk.full);
+    tl.r = r;
     return tl;
   };
   // per-lane byte offsets of the direct-to-LDS loads (A part does not depend on the tile)
@@ -338,6 +420,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
   // checks drop the ones outside C), so `pend`, the vector-memory operations
   // issued after an item's stage 0, is known when the item starts.
   constexpr bool EARLY = S == 2 && NW * EP_WAVE / 2 <= STAGE && TM % 2 == 0;
+  static_assert(!(INK && EARLY), "in-launch completion waits for all of the block's memory operations");
   constexpr int PART_ST = TM * TN * 4;  // float32 partial-sum stores per wave
   int pend = tl.kn > 1 ? NL : 0;
   auto wait_pend = [&](int n) {
@@ -541,6 +624,34 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(const bf16
             for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mi][ni][4 * gq + qq];
             *(f32x4*)(dst + ((int64_t)((mi * TN + ni) * 4 + gq) * (NW * kWave) + tid) * 4) = v;
           }
+      if constexpr (INK) {
+        // the block's partial sums are made visible to the device before it
+        // counts itself in (every wave's stores acknowledged, then one release
+        // by wave 0); the block that brings the count to the number of
+        // contributing blocks completes the tile and resets the count
+        wait_vmem<0>();
+        __syncthreads();
+        if (wave == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          const int ns = split_tile_slots(tl.r, sk.rem, nb, nk, xcd, s_slots);
+          if (lane == 0) {
+            int32_t* const ctr = counters + xcd * kSplitCountersPerXcd + tl.r;
+            const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old == ns - 1;
+            if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_done = last ? ns : 0;
+          }
+        }
+        __syncthreads();
+        const int ns = s_done;
+        if (ns > 0) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other blocks' partial sums
+          constexpr int NT = NW * kWave, PER = BM * BN / 4 / NT;
+          static_assert(PER * NT * 4 == BM * BN, "completion split");
+          complete_split_entries<BM, BN, WM, WN, PER, NT, 8, GELU>(partials, s_slots, ns, tid, C, tl.row0,
+                                                                  tl.row_end, tl.n0, N);
+        }
+      }
     } else {
       // ---- epilogue through LDS: each wave stages its WTM x WTN piece as bf16
       // in its own LDS region (row-major, 16-byte chunks XOR-swizzled by the
@@ -638,7 +749,6 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
                                                          bf16_bits* __restrict__ C, int64_t R, int nk, int N,
                                                          int E, int n_tiles, int nb, int min_steps,
                                                          int max_rem, int gm) {
-  constexpr int NW = WM * WN, WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
   constexpr int ENT = BM * BN / 4;           // float32x4 entries per slot
   constexpr int PER = ENT / SUB / 256;       // entries per thread
   static_assert(PER * SUB * 256 == ENT, "fixup split");
@@ -657,23 +767,10 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
   const int full = (hi - lo) / nb, rem = (hi - lo) - full * nb;
   if (!split_leftover(rem, nb, nk, min_steps, max_rem)) return;
   for (int r = r0; r < rem; r += rstep) {
-    const int64_t W = (int64_t)rem * nk, u0 = (int64_t)r * nk, u1 = u0 + nk;
-    // lane jj of wave 0 checks block jj's share [s0, s1) of the units (nb <= kMaxSlots = 64 lanes);
-    // the slots of the blocks that touch tile r, in block (= K) order
+    // the slots of the blocks that touch tile r, in block (= K) order (nb <= kMaxSlots = 64 lanes)
     if (threadIdx.x < kWave) {
-      const int jj = threadIdx.x;
-      bool touch = false, whole = false;
-      int slot = 0;
-      if (jj < nb) {
-        const int64_t s0 = W * jj / nb, s1 = W * (jj + 1) / nb;
-        touch = s1 > s0 && s0 < u1 && s1 > u0;
-        whole = touch && s0 <= u0 && s1 >= u1;  // one block ran the whole tile and stored it
-        slot = (jj * 8 + x) * 2 + (r - (int)(s0 / nk));
-      }
-      const uint64_t tm = __ballot(touch), wm = __ballot(whole);  // every lane of wave 0 votes
-      const int pos = __popcll(tm & ((1ull << jj) - 1ull));
-      if (touch) s_slots[pos] = slot;
-      if (jj == 0) s_nslots = wm ? -1 : __popcll(tm);
+      const int ns = split_tile_slots(r, rem, nb, nk, x, s_slots);
+      if (threadIdx.x == 0) s_nslots = ns;
     }
     __syncthreads();
     const int ns = s_nslots;
@@ -696,45 +793,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const int32_t* __restri
     const int64_t row_end = min((int64_t)offsets[e + 1], R);
     const int n0 = lanes::tile_n0(n_tile, n_tiles, N, BN);
 
-    f32x4 acc[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ebase = b * (ENT / SUB) + threadIdx.x;
-    // slots in K order, eight at a time so that their loads are in flight together
-    for (int si = 0; si < ns; si += 8) {
-      f32x4 v[8][PER];
-#pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const int sl = si + q4 < ns ? s_slots[si + q4] : -1;
-#pragma unroll
-        for (int u = 0; u < PER; ++u)
-          v[q4][u] = sl >= 0 ? ((const f32x4*)(partials + (int64_t)sl * (BM * BN)))[ebase + u * 256]
-                             : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4)
-#pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] += v[q4][u];
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      // entry -> (MFMA register group, thread) -> (row, 4 columns) of the tile
-      const int en = ebase + u * 256, grp = en / (NW * kWave), tt = en % (NW * kWave);
-      const int mi = grp / (TN * 4), ni = (grp / 4) % TN, gq = grp % 4;
-      const int wave = tt / kWave, lane = tt % kWave;
-      const int row = (wave / WN) * WTM + mi * 32 + (lane & 31);
-      const int col = (wave % WN) * WTN + ni * 32 + 8 * gq + 4 * (lane >> 5);
-      const int64_t grow = row0 + row;
-      const int n = n0 + col;
-      if (grow >= row_end || n < 0 || n >= N) continue;
-      float v[4];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) v[qq] = GELU ? gelu_tanh(acc[u][qq]) : acc[u][qq];
-      u32x2 o;
-      o[0] = pack_bf16x2(v[0], v[1]);
-      o[1] = pack_bf16x2(v[2], v[3]);
-      *(u32x2*)(C + grow * N + n) = o;
-    }
+    complete_split_entries<BM, BN, WM, WN, PER, 256, 8, GELU>(partials, s_slots, ns, b * (ENT / SUB) + threadIdx.x, C,
+                                                             row0, row_end, n0, N);
     __syncthreads();  // s_slots is rewritten for the next tile
   }
 }
@@ -872,9 +932,41 @@ int fixup_rounds() {
   return fr && fr[0] ? max(1, atoi(fr)) : kFixupRounds;
 }
 
+bool env_flag(const char* name) {
+  const char* f = getenv(name);
+  return f && f[0] && atoi(f) != 0;
+}
+
+// Whether a launch of the 32-row weight-streaming tile (a block per CU slot)
+// completes its split tiles itself (counters, no fixup launch) rather than in
+// a fixup launch. Each block that stores partial sums then writes back its
+// XCD's L2 before counting itself in, and one block sums the tile. Measured on
+// MI355X at 1..128 tokens of the four bf16 workloads: for the first GEMM this
+// is 1.5-3 us faster per layer once the batch holds at least E/2 rows (the
+// tile list then mostly fills whole rounds, and the fixup launch it saves has
+// little or nothing to do), ~5 us slower below that (tiles split over four or
+// more blocks); for the second GEMM (tiles split over 4-16 blocks) it is slower
+// at every size. MOE_GEMM_SPLIT_FIXUP=1 forces the fixup launch,
+// MOE_GEMM_SPLIT_INLAUNCH=1 the in-launch completion for both GEMMs.
+bool split_in_launch(int64_t R, int E, bool gelu) {
+  if (env_flag("MOE_GEMM_SPLIT_FIXUP")) return false;
+  if (env_flag("MOE_GEMM_SPLIT_INLAUNCH")) return true;
+  return gelu && 2 * R >= E;
+}
+
+template <int BM, int BN, int BK, int S, int OCC, int WM, int WN, bool GELU, bool GATHER, bool INK>
+void launch_kernel(unsigned grid, hipStream_t s, const void* A, const int32_t* offsets, const void* B, void* C,
+                   float* partials, int64_t R, int K, int N, int E, int n_tiles, int min_steps, int max_rem,
+                   const int32_t* perm, int64_t a_rows, int gm, int32_t* counters) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, GELU, GATHER, INK>), dim3(grid),
+                     dim3(WM * WN * 64), 0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C,
+                     partials, R, K, N, E, n_tiles, min_steps, max_rem, perm, a_rows, gm, counters);
+}
+
 template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2, bool FILL = false>
-hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials, int64_t R,
-                       int K, int N, int E, bool gelu, const int32_t* perm, int64_t a_rows, hipStream_t s) {
+hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials,
+                       int32_t* counters, int64_t R, int K, int N, int E, bool gelu, const int32_t* perm,
+                       int64_t a_rows, hipStream_t s) {
   const int n_tiles = (int)ceil_div(N, BN);
   const int64_t tiles_ub = tiles_upper_bound(R, N, E, BM, BN);
   if (tiles_ub > INT32_MAX || K % BK != 0) return hipErrorInvalidValue;
@@ -888,40 +980,37 @@ hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, voi
   // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
   const int max_rem = FILL ? nb - 1 : nb / 3;
   const int gm = group_m();
+  // a block per CU slot (decode-sized batches): split tiles may be completed inside the launch
+  const bool ink = FILL && split_in_launch(R, E, gelu);
+  if (ink && (!counters || max_rem > kSplitCountersPerXcd)) return hipErrorInvalidValue;
   // fixup blocks: FS per split tile, each looping over up to kFixupRounds tiles
   constexpr int FS = fixup_sub<BM, BN>();
   const int fix_r = (max_rem + fixup_rounds() - 1) / fixup_rounds();
-  const unsigned fix_grid = nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * FS) : 0u;
-  constexpr int NT = WM * WN * 64;
-  if (gelu && perm) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true, true>), dim3((unsigned)grid), dim3(NT), 0,
-                       s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, perm, a_rows, gm);
-    if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
-  } else if (perm) {  // the first GEMM without its activation (training keeps U = x W1)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false, true>), dim3((unsigned)grid), dim3(NT),
-                       0, s, (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, perm, a_rows, gm);
-    if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
-  } else if (gelu) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, true>), dim3((unsigned)grid), dim3(NT), 0, s,
-                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, nullptr, R, gm);
-    if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, true>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
+  const unsigned fix_grid = !ink && nk >= min_steps && max_rem > 0 ? (unsigned)(8 * fix_r * FS) : 0u;
+  const unsigned g = (unsigned)grid;
+#define MOE_LAUNCH(GELU_, GATHER_)                                                                              \
+  do {                                                                                                           \
+    if (ink)                                                                                                     \
+      launch_kernel<BM, BN, BK, S, OCC, WM, WN, GELU_, GATHER_, FILL>(g, s, A, offsets, B, C, partials, R, K, N, \
+                                                                      E, n_tiles, min_steps, max_rem, perm,      \
+                                                                      a_rows, gm, counters);                     \
+    else                                                                                                         \
+      launch_kernel<BM, BN, BK, S, OCC, WM, WN, GELU_, GATHER_, false>(g, s, A, offsets, B, C, partials, R, K,   \
+                                                                       N, E, n_tiles, min_steps, max_rem, perm,  \
+                                                                       a_rows, gm, nullptr);                     \
+    if (fix_grid)                                                                                                \
+      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, GELU_>), dim3(fix_grid), dim3(256), 0, s,        \
+                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps,    \
+                         max_rem, gm);                                                                           \
+  } while (0)
+  if (perm) {
+    if (gelu) MOE_LAUNCH(true, true);
+    else MOE_LAUNCH(false, true);  // the first GEMM without its activation (training keeps U = x W1)
   } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, OCC, WM, WN, false>), dim3((unsigned)grid), dim3(NT), 0, s,
-                       (const bf16_bits*)A, offsets, (const bf16_bits*)B, (bf16_bits*)C, partials, R, K, N, E,
-                       n_tiles, min_steps, max_rem, nullptr, R, gm);
-    if (fix_grid)
-      hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN, WM, WN, FS, false>), dim3(fix_grid), dim3(256), 0, s,
-                         offsets, (const float*)partials, (bf16_bits*)C, R, nk, N, E, n_tiles, nb, min_steps, max_rem, gm);
+    if (gelu) MOE_LAUNCH(true, false);
+    else MOE_LAUNCH(false, false);
   }
+#undef MOE_LAUNCH
   return hipGetLastError();
 }
 
@@ -1007,9 +1096,13 @@ size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
   return (size_t)grid * 2 * ts.bm * ts.bn * sizeof(float);  // two split segments per block at most
 }
 
+bool grouped_gemm_uses_counters(int dtype, int64_t R, int K, int N, int E, bool gelu) {
+  return dtype == MOE_DTYPE_BF16 && kShapes[pick_tile(R, K, N, E)].fill && split_in_launch(R, E, gelu);
+}
+
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
-                               const int32_t* perm, int64_t a_rows) {
+                               float* partials, int32_t* counters, int64_t R, int K, int N, int E, bool gelu,
+                               hipStream_t s, const int32_t* perm, int64_t a_rows) {
   if (perm && (dtype != MOE_DTYPE_BF16 || a_rows * K * 2 >= (int64_t)INT32_MAX))
     return hipErrorInvalidValue;  // row gathering: bf16, A addressable with 31-bit offsets
   if (dtype == MOE_DTYPE_F32) {
@@ -1027,22 +1120,29 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
   }
   switch (pick_tile(R, K, N, E)) {
     case 0:
-      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                             a_rows, s);
     case 1:
-      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                             a_rows, s);
     case 2:
-      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                             a_rows, s);
     case 3:
-      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                             a_rows, s);
     case 4:
-      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                             a_rows, s);
     case 5:
-      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                                   a_rows, s);
     case kDecodeTile:
-      return launch_bf16<32, 256, 64, 4, 1, 1, 4, true>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows,
-                                                        s);
+      return launch_bf16<32, 256, 64, 4, 1, 1, 4, true>(A, offsets, B, C, partials, counters, R, K, N, E, gelu,
+                                                        perm, a_rows, s);
     default:
-      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, R, K, N, E, gelu, perm, a_rows, s);
+      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+                                                   a_rows, s);
   }
 }
 

@@ -12,8 +12,10 @@ namespace moe {
 constexpr int kPermuteTokensPerBlock = 256;
 // batches of at most this many tokens (and k <= 8) are permuted by one workgroup
 constexpr int kSmallPermuteT = 1024;
-// ... and with at most this many, that workgroup also completes a split router
-constexpr int kFusedRouteT = 16;
+// ... and with at most kFusedTokens (kFusedRouteT at most), that workgroup
+// also completes a split router
+constexpr int kFusedRouteT = 32;
+constexpr int kFusedTokens = 16;
 
 inline int64_t permute_blocks(int64_t T) { return (T + kPermuteTokensPerBlock - 1) / kPermuteTokensPerBlock; }
 
@@ -35,15 +37,22 @@ hipError_t launch_route_partials(const moe_problem_t& p, const void* x, const vo
 // split router from its partial logits (idx, gate as launch_route would give
 // them) and permutes (counts, offsets, perm, inv as launch_permute_index).
 bool route_permute_fused(const moe_problem_t& p);
+// With `zero`, both permute launchers also set its first nzero (<= 1024)
+// int32 to 0 on the way (the grouped GEMMs' split-tile counters).
 hipError_t launch_finalize_permute_small(const moe_problem_t& p, const float* part, int nsplit, const float* bias,
                                         int32_t* idx, float* gate, int32_t* counts, int32_t* offsets,
-                                        int32_t* perm, int32_t* inv, hipStream_t s);
+                                        int32_t* perm, int32_t* inv, hipStream_t s, int32_t* zero = nullptr,
+                                        int nzero = 0);
 
 // counts/offsets/perm/inv from the routing table; blockcounts/blockbase are
 // workspace arrays of permute_blocks(T) * E int32 each.
 hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts,
                                 int32_t* offsets, int32_t* perm, int32_t* inv,
-                                int32_t* blockcounts, int32_t* blockbase, hipStream_t s);
+                                int32_t* blockcounts, int32_t* blockbase, hipStream_t s, int32_t* zero = nullptr,
+                                int nzero = 0);
+
+// p[0 .. n) = 0 (one small block)
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 
 // x_perm[inv[t*k+j]] = x[t] for every valid selection.
 hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* inv, void* x_perm,
@@ -54,9 +63,17 @@ hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* i
 // workspace of grouped_gemm_partials_bytes() for split tiles (bf16 path).
 // With `perm` (bf16) row r of A is row perm[r] of A [a_rows, K]; returns
 // hipErrorInvalidValue when a_rows * K * 2 does not fit in 31 bits.
+// `counters` (kGemmSplitCounters int32) must be zero when the launch starts
+// if grouped_gemm_uses_counters() says the launch completes split tiles
+// itself (gelu: the launch's activation); it leaves them zero again.
+// Launches on one stream may share them.
 hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets, const void* B, void* C,
-                               float* partials, int64_t R, int K, int N, int E, bool gelu, hipStream_t s,
-                               const int32_t* perm = nullptr, int64_t a_rows = 0);
+                               float* partials, int32_t* counters, int64_t R, int K, int N, int E, bool gelu,
+                               hipStream_t s, const int32_t* perm = nullptr, int64_t a_rows = 0);
+// split-tile counters: one per leftover tile of each XCD's range
+constexpr int kSplitCountersPerXcd = 64;
+constexpr int kGemmSplitCounters = 8 * kSplitCountersPerXcd;
+bool grouped_gemm_uses_counters(int dtype, int64_t R, int K, int N, int E, bool gelu);
 
 // Host-only bound of the partial-sum workspace one launch_grouped_gemm call may use.
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);

@@ -57,13 +57,23 @@ PermuteWs carve_permute(Carver& c, const moe_problem_t& p) {
 }
 
 struct FfnWs {
-  void* h;           // hidden activations [T*k, d_expert]
-  float* partials;   // split-tile partial sums of either GEMM
+  void* h;            // hidden activations [T*k, d_expert]
+  float* partials;    // split-tile partial sums of either GEMM
+  int32_t* counters;  // split-tile counters of either GEMM (zero between launches)
 };
+
+// whether the grouped GEMMs of the layer complete split tiles with counters
+// that must be zero when they start
+bool ffn_uses_counters(const moe_problem_t& p) {
+  const int64_t R = p.T * p.k;
+  return moe::grouped_gemm_uses_counters(p.dtype, R, p.d_model, p.d_expert, p.E, true) ||
+         moe::grouped_gemm_uses_counters(p.dtype, R, p.d_expert, p.d_model, p.E, false);
+}
 
 FfnWs carve_ffn(Carver& c, const moe_problem_t& p) {
   const int64_t R = p.T * p.k;
   FfnWs w;
+  w.counters = c.take<int32_t>(moe::kGemmSplitCounters);
   w.h = c.take<char>((size_t)R * p.d_expert * elem_size(p.dtype));
   const size_t pb = std::max(moe::grouped_gemm_partials_bytes(p.dtype, R, p.d_model, p.d_expert, p.E),
                              moe::grouped_gemm_partials_bytes(p.dtype, R, p.d_expert, p.d_model, p.E));
@@ -110,6 +120,7 @@ struct TrainWs {
   void *U, *H, *y_perm;                              // [R, d_expert] x2, [R, d_model] (bf16)
   PermuteWs pw;
   float *route_part, *partials;
+  int32_t* counters;                                 // split-tile counters of the forward GEMMs
   uint16_t* dwr_part;                                // [splits, d, E] bf16: x^T dlogit per token split
   void *dYp, *dU, *dXp, *dxr;                        // [R, d], [R, de], [R, d], [T, d] (bf16)
   float *dlogit, *prob, *stat_part;                  // [T, E], [T, E], [chunks, 2, E]
@@ -139,6 +150,7 @@ TrainWs carve_train(Carver& c, const moe_problem_t& p) {
                               moe::bwd_partials_bytes((int64_t)R, p.E, p.d_model),
                               (size_t)moe::kKGroupSlots * 256 * 256 * sizeof(float)});
   w.partials = c.take<float>(pb / sizeof(float));
+  w.counters = c.take<int32_t>(moe::kGemmSplitCounters);
   w.dwr_part = c.take<uint16_t>((size_t)moe::bwd_router_splits(p.T, p.d_model, p.E) * p.d_model * p.E);
   w.dYp = c.take<uint16_t>(R * p.d_model);
   w.dU = c.take<uint16_t>(R * p.d_expert);
@@ -274,11 +286,13 @@ MOE_API moe_status_t moe_grouped_ffn_gather(const moe_problem_t* p, const void* 
   const FfnWs fw = carve_ffn(c, *p);
   hipStream_t s = (hipStream_t)stream;
   const int64_t R = p->T * p->k;
-  hipError_t e = moe::launch_grouped_gemm(p->dtype, x, offsets, W1, fw.h, fw.partials, R, p->d_model,
-                                          p->d_expert, p->E, true, s, perm, p->T);
+  hipError_t e = ffn_uses_counters(*p) ? moe::launch_zero_i32(fw.counters, moe::kGemmSplitCounters, s) : hipSuccess;
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, x, offsets, W1, fw.h, fw.partials, fw.counters, R, p->d_model,
+                                 p->d_expert, p->E, true, s, perm, p->T);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, R, p->d_expert,
-                                             p->d_model, p->E, false, s));
+  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, fw.counters, R,
+                                             p->d_expert, p->d_model, p->E, false, s));
 }
 
 MOE_API moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
@@ -295,11 +309,13 @@ MOE_API moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x_perm,
   const FfnWs fw = carve_ffn(c, *p);
   hipStream_t s = (hipStream_t)stream;
   const int64_t R = p->T * p->k;
-  hipError_t e = moe::launch_grouped_gemm(p->dtype, x_perm, offsets, W1, fw.h, fw.partials, R, p->d_model,
-                                          p->d_expert, p->E, true, s);
+  hipError_t e = ffn_uses_counters(*p) ? moe::launch_zero_i32(fw.counters, moe::kGemmSplitCounters, s) : hipSuccess;
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm(p->dtype, x_perm, offsets, W1, fw.h, fw.partials, fw.counters, R, p->d_model,
+                                 p->d_expert, p->E, true, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, R, p->d_expert,
-                                             p->d_model, p->E, false, s));
+  return hip_status(moe::launch_grouped_gemm(p->dtype, fw.h, offsets, W2, y_perm, fw.partials, fw.counters, R,
+                                             p->d_expert, p->d_model, p->E, false, s));
 }
 
 MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* inv,
@@ -333,28 +349,29 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
     e = moe::launch_route_partials(*p, x, w_router, w.route_part, s);
     if (e == hipSuccess)
       e = moe::launch_finalize_permute_small(*p, w.route_part, moe::route_splits(*p), router_bias, w.idx, w.gate,
-                                             w.counts,
-                                             w.offsets, w.perm, w.inv, s);
+                                             w.counts, w.offsets, w.perm, w.inv, s, w.fw.counters,
+                                             moe::kGemmSplitCounters);
   } else {
     e = moe::launch_route(*p, x, w_router, router_bias, nullptr, w.idx, w.gate, w.route_part, s);
     if (e == hipSuccess)
       e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts,
-                                    w.pw.blockbase, s);
+                                    w.pw.blockbase, s, w.fw.counters, moe::kGemmSplitCounters);
   }
+  // (the permute launch also cleared the GEMMs' split-tile counters)
   if (gather_supported(*p)) {
     // dispatch folded into the first GEMM: its A rows are read as x[perm[r]]
     if (e == hipSuccess)
-      e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model, p->d_expert,
-                                   p->E, true, s, w.perm, p->T);
+      e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.fw.h, w.fw.partials, w.fw.counters, R, p->d_model,
+                                   p->d_expert, p->E, true, s, w.perm, p->T);
   } else {
     if (e == hipSuccess) e = moe::launch_gather(*p, x, w.inv, w.x_perm, s);
     if (e == hipSuccess)
-      e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.fw.h, w.fw.partials, R, p->d_model,
-                                   p->d_expert, p->E, true, s);
+      e = moe::launch_grouped_gemm(p->dtype, w.x_perm, w.offsets, W1, w.fw.h, w.fw.partials, w.fw.counters, R,
+                                   p->d_model, p->d_expert, p->E, true, s);
   }
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, w.fw.h, w.offsets, W2, w.y_perm, w.fw.partials, R, p->d_expert,
-                                 p->d_model, p->E, false, s);
+    e = moe::launch_grouped_gemm(p->dtype, w.fw.h, w.offsets, W2, w.y_perm, w.fw.partials, w.fw.counters, R,
+                                 p->d_expert, p->d_model, p->E, false, s);
   if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
   return hip_status(e);
 }
@@ -382,15 +399,15 @@ MOE_API moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, co
   hipError_t e = moe::launch_route(*p, x, w_router, router_bias, w.logits, w.idx, w.gate, w.route_part, s);
   if (e == hipSuccess)
     e = moe::launch_permute_index(*p, w.idx, w.counts, w.offsets, w.perm, w.inv, w.pw.blockcounts,
-                                  w.pw.blockbase, s);
+                                  w.pw.blockbase, s, w.counters, moe::kGemmSplitCounters);
   // U = x W1 per expert (rows read through perm), kept; H = GELU_tanh(U)
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.U, w.partials, R, p->d_model, p->d_expert, p->E,
-                                 false, s, w.perm, p->T);
+    e = moe::launch_grouped_gemm(p->dtype, x, w.offsets, W1, w.U, w.partials, w.counters, R, p->d_model,
+                                 p->d_expert, p->E, false, s, w.perm, p->T);
   if (e == hipSuccess) e = moe::launch_gelu_rows(w.U, w.H, R * p->d_expert, s);
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm(p->dtype, w.H, w.offsets, W2, w.y_perm, w.partials, R, p->d_expert, p->d_model,
-                                 p->E, false, s);
+    e = moe::launch_grouped_gemm(p->dtype, w.H, w.offsets, W2, w.y_perm, w.partials, w.counters, R, p->d_expert,
+                                 p->d_model, p->E, false, s);
   if (e == hipSuccess) e = moe::launch_combine(*p, w.y_perm, w.inv, w.gate, y, s);
   return hip_status(e);
 }

@@ -54,8 +54,11 @@ __device__ __forceinline__ void build_mask(const int32_t* __restrict__ idx, int6
 }
 
 __global__ __launch_bounds__(kTB) void hist_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
-                                                   int32_t* __restrict__ blockcounts) {
+                                                   int32_t* __restrict__ blockcounts, int32_t* __restrict__ zero,
+                                                   int nzero) {
   __shared__ uint32_t mask[256][kWords];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += kTB) zero[i] = 0;
   build_mask(idx, T, k, E, mask, (int64_t)blockIdx.x * kTB);
   const int e = threadIdx.x;
   if (e < E) {
@@ -237,10 +240,10 @@ __global__ __launch_bounds__(kTB) void scatter_kernel(const int32_t* __restrict_
 constexpr int kSmallWords = kSmallPermuteT / 32;  // mask words per expert
 constexpr int kSmallThreads = 1024;
 static_assert(kSmallPermuteT <= kSmallThreads, "one token per thread");
-static_assert(kFusedRouteT <= kSmallThreads / kWave, "one token per wave");
+static_assert(kFusedRouteT <= 2 * kSmallThreads / kWave, "at most two tokens per wave");
 
 // One workgroup, T <= kSmallPermuteT tokens (thread t owns token t), k <= 8.
-// FIN (T <= kFusedRouteT, one token per wave): the routing of the batch is
+// FIN (T <= kFusedRouteT, one or two tokens per wave): the routing of the batch is
 // completed first, as the router's own finalize launch does it
 // (sum_partial_logits, then select_topk), so idx and gates are bitwise the
 // same; idx stays in LDS until the end, gates go out directly. Otherwise idx is read
@@ -251,8 +254,10 @@ template <bool FIN>
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ idx_in, const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
     float* __restrict__ gate, int32_t* __restrict__ idx_out, int T, int k, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ zero, int nzero) {
   __shared__ uint32_t mask[256][kSmallWords];
+  if ((int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   __shared__ int32_t s_idx[kSmallPermuteT * 8];
   __shared__ float lg[FIN ? kFusedRouteT : 1][256];
   __shared__ int32_t s_scan[256];
@@ -263,9 +268,10 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
   uint32_t* flat = &mask[0][0];
   for (int i = tid; i < E * kSmallWords; i += kSmallThreads) flat[i] = 0u;
   if constexpr (FIN) {
-    if (wave < T) {  // T <= kFusedRouteT = the workgroup's waves: one token each
-      sum_partial_logits(part, nsplit, bias, T, E, wave, lg[wave]);
-      select_topk(lg[wave], E, k, wave, nullptr, s_idx, gate);
+    // T <= kFusedRouteT: token t goes to wave t mod (the workgroup's waves), with an LDS row of its own
+    for (int t = wave; t < T; t += kSmallThreads / kWave) {
+      sum_partial_logits(part, nsplit, bias, T, E, t, lg[t]);
+      select_topk(lg[t], E, k, t, nullptr, s_idx, gate);
     }
   } else {
     for (int i = tid; i < P; i += kSmallThreads) s_idx[i] = idx_in[i];
@@ -366,21 +372,31 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_kernel(const u32x
 
 }  // namespace
 
+// Batches of at most kFusedTokens tokens complete a split router inside the
+// one-workgroup permute (MOE_FUSED_ROUTE_T=<n> overrides, at most kFusedRouteT).
+int fused_route_tokens() {
+  const char* f = getenv("MOE_FUSED_ROUTE_T");
+  return f && f[0] ? std::min(std::max(atoi(f), 0), kFusedRouteT) : kFusedTokens;
+}
+
 bool route_permute_fused(const moe_problem_t& p) {
   const int ns = route_splits(p);
-  return ns > 1 && p.T <= kFusedRouteT && p.k <= 8 && (int64_t)ns * p.T * p.E * 4 <= 256 * 1024;
+  return ns > 1 && p.T <= fused_route_tokens() && p.k <= 8 && (int64_t)ns * p.T * p.E * 4 <= 256 * 1024;
 }
 
 hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* inv, int32_t* blockcounts, int32_t* blockbase,
-                                hipStream_t s) {
+                                hipStream_t s, int32_t* zero, int nzero) {
+  if (!zero) nzero = 0;
+  if (nzero < 0 || nzero > kSmallThreads) return hipErrorInvalidValue;
   if (p.T <= kSmallPermuteT && p.k <= 8) {
     hipLaunchKernelGGL(permute_small_kernel<false>, dim3(1), dim3(kSmallThreads), 0, s, idx, nullptr, 0, nullptr,
-                       nullptr, nullptr, (int)p.T, p.k, p.E, counts, offsets, perm, inv);
+                       nullptr, nullptr, (int)p.T, p.k, p.E, counts, offsets, perm, inv, zero, nzero);
     return hipGetLastError();
   }
   const int64_t nb = permute_blocks(p.T);
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts);
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts, zero,
+                     nzero);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // MOE_PERMUTE_FUSED_SCAN=0|1 forces the choice (1 only within kFusedScanBlocks)
@@ -403,10 +419,23 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
 
 hipError_t launch_finalize_permute_small(const moe_problem_t& p, const float* part, int nsplit, const float* bias,
                                         int32_t* idx, float* gate, int32_t* counts, int32_t* offsets,
-                                        int32_t* perm, int32_t* inv, hipStream_t s) {
-  if (p.T > kFusedRouteT || p.k > 8 || p.E % 4 != 0) return hipErrorInvalidValue;
+                                        int32_t* perm, int32_t* inv, hipStream_t s, int32_t* zero, int nzero) {
+  if (!zero) nzero = 0;
+  if (p.T > kFusedRouteT || p.k > 8 || p.E % 4 != 0 || nzero < 0 || nzero > kSmallThreads)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(permute_small_kernel<true>, dim3(1), dim3(kSmallThreads), 0, s, nullptr, part, nsplit, bias,
-                     gate, idx, (int)p.T, p.k, p.E, counts, offsets, perm, inv);
+                     gate, idx, (int)p.T, p.k, p.E, counts, offsets, perm, inv, zero, nzero);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

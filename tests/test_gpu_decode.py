@@ -7,6 +7,8 @@ second launch) and the 32-row GEMM tile with a block per CU slot, whose one
 partly filled round of weight slabs is split over all blocks by K steps.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -53,3 +55,31 @@ def test_forward_decode_sized(moe, name, T, k):
     err = rel_err(f64(y)[keep], ref["y"][keep])
     print(f"{cfg.name} T={T} k={cfg.k}: y rel err {err:.3e}, near-ties excluded {int((~keep).sum())}")
     assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("mode", ["default", "inlaunch"])
+@pytest.mark.parametrize("name,T", [("mixtral_coarse", 1), ("mixtral_coarse", 32), ("fine_grained", 8),
+                                    ("skewed", 33)])
+def test_decode_split_completion_in_launch(moe, name, T, mode):
+    """moe_forward at decode sizes with split tiles completed inside the GEMM
+    launches (the library's choice per GEMM, or forced for both): y equals,
+    bit for bit, the layer run with fixup launches, on three calls in a row."""
+    cfg = scaled_config(name, T=T, suffix="decode")
+    announce(f"forward decode in-launch completion {cfg.name} T={cfg.T}")
+    inp = make_inputs(cfg, seed=6, device="cuda")
+    layer = moe.MoEForward(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, inp["x"].dtype)
+    args = (inp["x"], inp["w_router"], inp["W1"], inp["W2"], inp["router_bias"])
+    os.environ["MOE_GEMM_SPLIT_FIXUP"] = "1"
+    try:
+        ref = layer(*args).clone()
+    finally:
+        del os.environ["MOE_GEMM_SPLIT_FIXUP"]
+    if mode == "inlaunch":
+        os.environ["MOE_GEMM_SPLIT_INLAUNCH"] = "1"
+    try:
+        ys = [layer(*args).clone() for _ in range(3)]
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("MOE_GEMM_SPLIT_INLAUNCH", None)
+    for i, y in enumerate(ys):
+        assert torch.equal(y, ref), i

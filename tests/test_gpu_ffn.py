@@ -219,3 +219,50 @@ def test_fixup_rounds_do_not_change_results(moe, blocks):
     assert torch.equal(out["2"], out["1"]) and torch.equal(out["4"], out["1"])
     ref = oracle_ffn("bf16", x, off.cpu(), W1, W2)
     assert rel_err(f64(out["4"]), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("blocks", [24, 64, 256])
+def test_split_completion_in_launch_matches_fixup(moe, blocks):
+    """The 32-row weight-streaming tile can complete its split tiles inside
+    the GEMM launch (forced here for both GEMMs): the last block to store a
+    tile's partial sums adds all of its slots in K order. Outputs equal those
+    of the fixup launch bit for bit, for both FFN entry points and on three
+    calls in a row (each launch leaves its tile counters at zero for the next)."""
+    R, d, de, E = 3001, 512, 768, 7
+    announce(f"ffn split completion in launch blocks={blocks}")
+    x = make_dense((R, d), 1.0, seed=15, tag=1, device="cuda")
+    W1 = make_dense((E, d, de), d ** -0.5, seed=15, tag=2, device="cuda")
+    W2 = make_dense((E, de, d), de ** -0.5, seed=15, tag=3, device="cuda")
+    off = make_group_offsets(E, R, seed=15, empty=(2,)).cuda()
+    perm = torch.randperm(R, generator=torch.Generator().manual_seed(15)).to(torch.int32).cuda()
+    p = moe.make_problem(R, d, E, 1, de, "bf16")
+
+    def both():
+        y = run_ffn(moe, R, d, de, E, "bf16", x, off, W1, W2)
+        ws = torch.empty(moe.moe_workspace_size(p, moe.MOE_STAGE_GROUPED_FFN), dtype=torch.uint8, device="cuda")
+        yg = torch.full_like(y, float("nan"))
+        moe.moe_grouped_ffn_gather(p, x, perm, off, W1, W2, yg, ws)
+        torch.cuda.synchronize()
+        return y, yg
+
+    env = {"MOE_GEMM_TILE": "32x256", "MOE_GEMM_MAX_BLOCKS": str(blocks), "MOE_GEMM_SPLIT_MIN_STEPS": "0"}
+    os.environ.update(env)
+    try:
+        os.environ["MOE_GEMM_SPLIT_FIXUP"] = "1"
+        ref = both()
+        del os.environ["MOE_GEMM_SPLIT_FIXUP"]
+        os.environ["MOE_GEMM_SPLIT_INLAUNCH"] = "1"
+        runs = [both() for _ in range(3)]
+    finally:
+        os.environ.pop("MOE_GEMM_SPLIT_FIXUP", None)
+        os.environ.pop("MOE_GEMM_SPLIT_INLAUNCH", None)
+        for k in env:
+            del os.environ[k]
+    for i, (y, yg) in enumerate(runs):
+        assert torch.equal(y, ref[0]), i
+        assert torch.equal(yg, ref[1]), i
+    xr = oracle.decode(host_array(x), "bf16")[host_array(perm).astype(np.int64)]
+    w1, w2 = host_array(W1), host_array(W2)
+    want = oracle.grouped_ffn(xr, host_array(off), lambda e: oracle.decode(w1[e], "bf16"),
+                              lambda e: oracle.decode(w2[e], "bf16"))
+    assert rel_err(f64(runs[2][1]), want) <= TOL_BF16
