@@ -261,7 +261,34 @@ def phase_times(moe, cfg, layer, x, wr, b, W1, W2, warmup, steps, stream, dev):
         stage_step(events[s])
     torch.cuda.synchronize()
     ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, n in enumerate(PHASE_NAMES)}
-    return {"ms": ms, "gather": gather, "y": bufs["y"], "used_experts": int((bufs["counts"] > 0).sum().item())}
+    counts = bufs["counts"].cpu()
+    return {"ms": ms, "gather": gather, "y": bufs["y"], "used_experts": int((counts > 0).sum().item()),
+            "counts": [int(c) for c in counts.tolist()]}
+
+
+def cost_model_check(moe, cfg, counts, ms_step, phase_ms):
+    """The per-phase cost model's prediction for this workload from the routed
+    counts of the timed inputs, against the measured step and phases."""
+    from sparse_mixture_experts_route_amd import cost_model
+    if cfg.dtype != "bf16":
+        return None
+    pr = cost_model.calibrated().predict(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, counts)
+    return {"predicted_ms_per_step": round(pr["step"] / 1e3, 4),
+            "err_vs_step": round(pr["step"] / 1e3 / ms_step - 1.0, 4),
+            "predicted_phases_ms": {n: round(pr[n] / 1e3, 4) for n in PHASE_NAMES},
+            "err_vs_phases": {n: round(pr[n] / 1e3 / phase_ms[n] - 1.0, 4) for n in PHASE_NAMES}}
+
+
+def ffn_kernels(moe, cfg):
+    """The grouped-FFN phase's launches as the library plans them."""
+    plan = moe.moe_plan(moe.make_problem(cfg.T, cfg.d_model, cfg.E, cfg.k, cfg.d_expert, cfg.dtype))
+    if cfg.dtype != "bf16":
+        return "gemm_f32_kernel x2"
+    names = {5: "256x256w8", 7: "32x256"}
+    fix = sum(1 for g in plan["gemm"]
+              if not g["split_in_launch"] and g["k_steps"] >= g["min_steps"] and g["max_split"] > 0)
+    tiles = "/".join(names.get(g["tile"], str(g["tile"])) for g in plan["gemm"])
+    return f"gemm_bf16_kernel x2 (tiles {tiles}) + gemm_fixup_kernel x{fix}"
 
 
 def extra_config(moe, cfg, args, stream, dev):
@@ -283,7 +310,8 @@ def extra_config(moe, cfg, args, stream, dev):
            "phases_ms": {n: round(v, 4) for n, v in ph["ms"].items()},
            "ffn_tflops": round(ffn_tflops, 2),
            "ffn_frac_of_bf16_peak": round(ffn_tflops / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
-           "phase_sum_over_step": round(sum(ph["ms"].values()) / head["ms"], 4)}
+           "phase_sum_over_step": round(sum(ph["ms"].values()) / head["ms"], 4),
+           "cost_model": cost_model_check(moe, cfg, ph["counts"], head["ms"], ph["ms"])}
     del inp, x, wr, b, W1, W2, layer, ph
     torch.cuda.empty_cache()
     return out
@@ -308,7 +336,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.5,
                     help="untimed whole-layer steps for this long before the warm-up (clocks reach steady state)")
-    ap.add_argument("--extra-configs", default="fine_grained,large_sparse",
+    ap.add_argument("--extra-configs", default="fine_grained,skewed,large_sparse",
                     help="other workloads whose tokens/s and FFN TFLOP/s are added to the line ('' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size kernel "
@@ -375,15 +403,14 @@ def main():
         gbs = bytes_["ffn"] / t_ffn / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                    "kernel": f"grouped FFN phase: gemm_bf16_kernel x2 (32x256 weight-streaming tile) + "
-                              f"gemm_fixup_kernel x2; bytes = weights of the {used} experts with tokens "
-                              f"+ activations"}
+                    "kernel": f"grouped FFN phase: {ffn_kernels(moe, cfg)}; bytes = weights of the {used} "
+                              f"experts with tokens + activations"}
     elif cfg.dtype == "bf16":
         roofline = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(cfg.name),
-                    "kernel": "grouped FFN phase: gemm_bf16_kernel x2 (GEMM1+GELU reading x through perm, GEMM2)"
-                              " + gemm_fixup_kernel x2"}
+                    "kernel": f"grouped FFN phase: {ffn_kernels(moe, cfg)} (GEMM1+GELU reading x through "
+                              f"perm, GEMM2)"}
     else:
         gbs = bytes_["ffn"] / t_ffn / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -425,6 +452,7 @@ def main():
         "phase_sum_over_step": round(phase_sum / ms_step, 4),
         "phases_consistent": consistent,
         "roofline": roofline,
+        "cost_model": cost_model_check(moe, cfg, ph["counts"], ms_step, phase_ms),
         "settle_s": round(settle_s, 2),
         "wall_s_timed_region": round(head["wall"], 4),
         "gpu": torch.cuda.get_device_name(dev),

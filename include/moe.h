@@ -79,6 +79,48 @@ typedef struct {
  * moe_forward_train and moe_backward share one MOE_STAGE_TRAIN workspace. */
 moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t stage, size_t* bytes);
 
+/* The launch plan the library picks for problem p, for callers that model or
+ * check the layer's performance (the MOSAIC summary's operator-level
+ * performance model, method item 2, costs each operator from exactly these
+ * choices). Host only: enqueues nothing and reads no device memory; it may
+ * query the current device's compute-unit count, as the launchers do.
+ * Environment overrides that the launchers honour are honoured here too.
+ *   host_counts  NULL, or E int32 selections per expert in HOST memory (e.g. a
+ *                copy of moe_permute's counts): then each grouped GEMM's tile
+ *                list is given as the kernels derive it from the offsets
+ *   plan         HOST pointer, written on success
+ * MOE_ERR_INVALID_ARGUMENT for a bad problem or negative counts. */
+typedef struct {
+  int32_t tile;            /* block tile: 0 256x256, 1 256x256k32, 2 256x128, 3 128x128,
+                              4 128x128k32, 5 256x256w8, 6 256x256w8k32, 7 32x256 */
+  int32_t bm, bn, bk;      /* block tile rows, columns and K step */
+  int32_t grid;            /* persistent blocks (a multiple of 8, dealt to 8 XCDs) */
+  int32_t k_steps;         /* K steps of a whole tile */
+  int32_t max_split;       /* leftover tiles per XCD that may be split by K steps */
+  int32_t min_steps;       /* ... only when the split saves at least this many K steps */
+  int32_t split_in_launch; /* 1: split tiles completed inside the launch, 0: by a fixup launch */
+  /* with host_counts (else -1): */
+  int64_t tiles;           /* tiles of the launch */
+  int32_t xcd_rounds;      /* whole rounds of the XCD with the most tiles */
+  int32_t xcd_leftover;    /* its leftover tiles */
+  int32_t xcd_split;       /* 1 if that leftover is split over its blocks */
+  int32_t split_xcds;      /* XCDs whose leftover is split */
+} moe_gemm_plan_t;
+
+typedef struct {
+  int32_t route_splits;           /* router contraction split over d_model (1: one pass) */
+  int32_t route_tokens_per_block; /* 32 or 64 */
+  int32_t route_fused_permute;    /* 1: moe_forward's permute workgroup completes the split router */
+  int32_t permute_form;           /* 0 one workgroup, 1 histograms + self-scanning scatter,
+                                     2 histograms + scan launch + scatter */
+  int32_t gather_in_gemm;         /* 1: moe_forward folds the dispatch into the first GEMM */
+  int32_t combine_streaming;      /* 1: y_perm and y streamed with non-temporal accesses */
+  moe_gemm_plan_t gemm[2];        /* first (x W1, GELU) and second (H W2) grouped GEMM;
+                                     every field -1 for float32 problems */
+} moe_plan_t;
+
+moe_status_t moe_plan(const moe_problem_t* p, const int32_t* host_counts, moe_plan_t* plan);
+
 /* Router Linear + Softmax + top-k (blog section 3, structure: the gating
  * network is a Linear layer and a Softmax; only the top-k experts are used).
  *   x            [T, d_model]      input tokens

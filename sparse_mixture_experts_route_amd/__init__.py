@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     moe_permute,
     moe_permute_index,
     moe_permute_index_noalloc,
+    moe_plan,
     moe_route,
     moe_route_ws,
     moe_status_str,

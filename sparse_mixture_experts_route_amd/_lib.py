@@ -32,6 +32,19 @@ class Problem(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_expert", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class GemmPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("tile", "bm", "bn", "bk", "grid", "k_steps", "max_split",
+                                              "min_steps", "split_in_launch")] + \
+               [("tiles", ctypes.c_int64)] + \
+               [(n, ctypes.c_int32) for n in ("xcd_rounds", "xcd_leftover", "xcd_split", "split_xcds")]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("route_splits", "route_tokens_per_block", "route_fused_permute",
+                                              "permute_form", "gather_in_gemm", "combine_streaming")] + \
+               [("gemm", GemmPlan * 2)]
+
+
 def _load():
     if not os.path.exists(_LIB_FILE):
         raise ImportError(f"{_LIB_FILE} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -40,6 +53,7 @@ def _load():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sigs = {
         "moe_workspace_size": [P, i32, ctypes.POINTER(sz)],
+        "moe_plan": [P, vp, ctypes.POINTER(Plan)],
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp],
         "moe_route_ws": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -110,6 +124,23 @@ def moe_workspace_size(p: Problem, stage: int) -> int:
     out = ctypes.c_size_t(0)
     _check(_lib.moe_workspace_size(ctypes.byref(p), int(stage), ctypes.byref(out)), "moe_workspace_size")
     return int(out.value)
+
+
+def moe_plan(p: Problem, counts=None) -> dict:
+    """The launch plan of problem p (host only). counts: E per-expert selection
+    counts (any int sequence or CPU tensor) for the GEMMs' tile lists, or None."""
+    buf = None
+    if counts is not None:
+        vals = [int(c) for c in (counts.tolist() if isinstance(counts, torch.Tensor) else counts)]
+        if len(vals) != p.E:
+            raise ValueError("counts must hold E entries")
+        buf = (ctypes.c_int32 * p.E)(*vals)
+    out = Plan()
+    _check(_lib.moe_plan(ctypes.byref(p), ctypes.cast(buf, ctypes.c_void_p) if buf is not None else None,
+                         ctypes.byref(out)), "moe_plan")
+    d = {n: getattr(out, n) for n, _ in Plan._fields_ if n != "gemm"}
+    d["gemm"] = [{n: getattr(g, n) for n, _ in GemmPlan._fields_} for g in out.gemm]
+    return d
 
 
 def moe_route(p: Problem, x, w_router, router_bias, logits, topk_idx, topk_gate, stream=None):

@@ -21,13 +21,15 @@ the kernels' own work and schedule, so the constants are a least-squares fit:
             scan launch, more than 64 blocks of 256 tokens] + b3 * M
             selections (index arrays only: the token rows reach the first
             GEMM through perm)
-  ffn       per grouped GEMM: f0 + f1 * K steps of 64 run by the busiest
-            persistent block of a matrix-core tile + f2 * tiles that block
-            runs + f3 * MB of split-tile partial sums written and read back
-            + f4 * K steps of the busiest block of the 32-row weight-streaming
-            tile (f0 comes out negative: the step count charges in full the
-            first and last steps of a tile, which the pipeline overlaps with
-            its neighbours)
+  ffn       f0 * launches (each GEMM, and its fixup unless split tiles are
+            completed inside the launch or K is too short to split) + f1 * K
+            steps of 64 run by the busiest persistent block of a matrix-core
+            tile + f2 * tiles that block runs + f3 * MB of split-tile partial
+            sums written and read back + f4 * K steps of the busiest block of
+            the 32-row weight-streaming tile + f5 * MB of weight slabs that
+            tile streams (the experts with rows). f0 comes out near zero: the
+            step count charges in full the first and last steps of a tile,
+            which the pipeline overlaps with its neighbours
   combine   c0 + c1 * MB read and written (plain accesses) + c2 * MB read
             and written (non-temporal, y_perm of 128 MB or more) + c3 *
             thousands of elements one token's wave reads (k rows of d_model:
@@ -125,14 +127,14 @@ def pick_tile(R: int, K: int, N: int, E: int) -> int:
     return best
 
 
-def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, float]:
-    """Work of the busiest persistent block of one grouped-GEMM launch: K
-    steps of 64 in units of the 8-wave 256 x 256 tile (scaled by the tile's
-    MAC count, blocks sharing a CU and matrix-core efficiency), tiles begun,
-    split partial sums moved, and K steps of the weight-streaming tile."""
+def gemm_plan(counts: Sequence[int], K: int, N: int, E: int, gelu: bool) -> Dict[str, int]:
+    """One grouped GEMM launch as the library plans it (the fields of
+    moe_gemm_plan_t): tile, persistent grid (8 XCDs x blocks), K steps, the
+    split rule, in-launch completion of split tiles, and the tile list of
+    these per-expert counts dealt to the XCDs in contiguous eighths."""
     R = sum(counts)
     shape = pick_tile(R, K, N, E)
-    _, bm, bn, bk, occ, eff = SHAPES[shape]
+    _, bm, bn, bk, occ, _ = SHAPES[shape]
     stream = shape == DECODE_TILE
     n_t = math.ceil(N / bn)
     tiles = sum(math.ceil(c / bm) for c in counts) * n_t
@@ -140,9 +142,27 @@ def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, floa
     grid = CUS * occ if stream else max(8, min(math.ceil(tiles_ub / 8) * 8, CUS * occ))
     nb = grid // 8
     nk = K // bk
-    tx = math.ceil(tiles / 8)  # tiles of the fullest XCD (each XCD takes a contiguous eighth)
-    full, rem = divmod(tx, nb)
-    if _split(rem, nb, nk, nb - 1 if stream else None):
+    max_rem = nb - 1 if stream else nb // 3
+    xcd = [tiles * (x + 1) // 8 - tiles * x // 8 for x in range(8)]
+    full, rem = divmod(max(xcd), nb)
+    return {"tile": shape, "bm": bm, "bn": bn, "bk": bk, "grid": grid, "k_steps": nk, "max_split": max_rem,
+            "min_steps": SPLIT_MIN_STEPS, "split_in_launch": int(stream and gelu and 2 * R >= E),
+            "tiles": tiles, "xcd_rounds": full, "xcd_leftover": rem,
+            "xcd_split": int(_split(rem, nb, nk, max_rem)),
+            "split_xcds": sum(int(_split(t % nb, nb, nk, max_rem)) for t in xcd)}
+
+
+def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int, gelu: bool) -> Dict[str, float]:
+    """Work of the busiest persistent block of one grouped-GEMM launch: K
+    steps of 64 in units of the 8-wave 256 x 256 tile (scaled by the tile's
+    MAC count, blocks sharing a CU and matrix-core efficiency), tiles begun,
+    split partial sums moved, K steps of the weight-streaming tile, and the
+    fixup launch (absent when split tiles are completed inside the launch)."""
+    g = gemm_plan(counts, K, N, E, gelu)
+    _, bm, bn, bk, occ, eff = SHAPES[g["tile"]]
+    stream = g["tile"] == DECODE_TILE
+    nb, nk, full, rem = g["grid"] // 8, g["k_steps"], g["xcd_rounds"], g["xcd_leftover"]
+    if g["xcd_split"]:
         steps = full * nk + math.ceil(rem * nk / nb)
         n_tiles = full + 1
         partial_mb = 2 * 8 * nb * bm * bn * 4 / 1e6  # every block writes a share, the fixup reads it
@@ -150,10 +170,15 @@ def _gemm_terms(counts: Sequence[int], K: int, N: int, E: int) -> Dict[str, floa
         n_tiles = full + (1 if rem else 0)
         steps = n_tiles * nk
         partial_mb = 0.0
+    fixup = 0.0 if g["split_in_launch"] or not (nk >= SPLIT_MIN_STEPS and g["max_split"] > 0) else 1.0
     if stream:
-        return {"steps": 0.0, "tiles": n_tiles, "partial_mb": partial_mb, "stream_steps": steps}
+        # the weight slabs of the experts with rows, streamed once from HBM
+        weight_mb = sum(1 for c in counts if c > 0) * K * N * 2 / 1e6
+        return {"steps": 0.0, "tiles": n_tiles, "partial_mb": partial_mb, "stream_steps": steps, "fixup": fixup,
+                "stream_mb": weight_mb}
     scale = (bm * bn * bk * occ) / (256 * 256 * 64) / eff
-    return {"steps": steps * scale, "tiles": n_tiles * occ, "partial_mb": partial_mb, "stream_steps": 0.0}
+    return {"steps": steps * scale, "tiles": n_tiles * occ, "partial_mb": partial_mb, "stream_steps": 0.0,
+            "fixup": fixup, "stream_mb": 0.0}
 
 
 def route_rt(T: int, E: int) -> int:
@@ -184,6 +209,30 @@ def _route_blocks_per_cu(ep: int, rt: int = 64) -> int:
 
 
 COMBINE_STREAM_BYTES = 128 << 20  # y_perm size from which the combine streams (non-temporal accesses)
+FUSED_ROUTE_T = 16  # tokens up to which moe_forward's permute workgroup completes a split router
+
+
+def plan(T: int, d_model: int, E: int, k: int, d_expert: int, counts: Optional[Sequence[int]] = None) -> Dict:
+    """The bf16 layer's launch decisions as this model restates them, in the
+    form of the library's moe_plan (include/moe.h): router split and block,
+    permute form, combine mode and both grouped GEMMs (their tile lists only
+    with counts). The tests hold the two equal."""
+    R = T * k
+    ns = route_splits(T, d_model, E)
+    small = T <= 1024 and k <= 8
+    out = {"route_splits": ns, "route_tokens_per_block": route_rt(T, E),
+           "route_fused_permute": int(ns > 1 and T <= FUSED_ROUTE_T and k <= 8 and ns * T * E * 4 <= 256 * 1024),
+           "permute_form": 0 if small else (1 if math.ceil(T / 256) <= 64 else 2),
+           "gather_in_gemm": int(T * d_model * 2 < 2 ** 31 - 1),
+           "combine_streaming": int(R * d_model * 2 >= COMBINE_STREAM_BYTES)}
+    c = list(counts) if counts is not None else balanced_counts(T, E, k)
+    gemms = [gemm_plan(c, d_model, d_expert, E, True), gemm_plan(c, d_expert, d_model, E, False)]
+    if counts is None:
+        for g in gemms:
+            for key in ("tiles", "xcd_rounds", "xcd_leftover", "xcd_split", "split_xcds"):
+                g[key] = -1
+    out["gemm"] = gemms
+    return out
 
 
 def features(s: Sample) -> Dict[str, np.ndarray]:
@@ -192,21 +241,22 @@ def features(s: Sample) -> Dict[str, np.ndarray]:
     R = T * k
     es = 2
     ep = math.ceil(E / 64) * 64
-    ns = route_splits(T, d, E)
-    rt = route_rt(T, E)
+    pl = plan(T, d, E, k, de)
+    ns, rt = pl["route_splits"], pl["route_tokens_per_block"]
     rounds = math.ceil(math.ceil(T / rt) * ns / (CUS * _route_blocks_per_cu(ep, rt)))
     chain = rounds * math.ceil(d / 64 / ns)
-    small = 1.0 if T <= 1024 and k <= 8 else 0.0
-    scan_launch = 1.0 if not small and math.ceil(T / 256) > 64 else 0.0
+    small = 1.0 if pl["permute_form"] == 0 else 0.0
+    scan_launch = 1.0 if pl["permute_form"] == 2 else 0.0
     mb = (R * d * es + T * d * es) / 1e6
-    stream = R * d * es >= COMBINE_STREAM_BYTES
-    g1 = _gemm_terms(s.counts, d, de, E)
-    g2 = _gemm_terms(s.counts, de, d, E)
+    stream = pl["combine_streaming"]
+    g1 = _gemm_terms(s.counts, d, de, E, True)
+    g2 = _gemm_terms(s.counts, de, d, E, False)
     return {
         "route": np.array([1.0, chain, chain * ep / 64, (ns * E / 1e3) if ns > 1 else 0.0, R / 1e6]),
         "permute": np.array([1.0, small, scan_launch, R / 1e6]),
-        "ffn": np.array([2.0, g1["steps"] + g2["steps"], g1["tiles"] + g2["tiles"],
-                         g1["partial_mb"] + g2["partial_mb"], g1["stream_steps"] + g2["stream_steps"]]),
+        "ffn": np.array([2.0 + g1["fixup"] + g2["fixup"], g1["steps"] + g2["steps"], g1["tiles"] + g2["tiles"],
+                         g1["partial_mb"] + g2["partial_mb"], g1["stream_steps"] + g2["stream_steps"],
+                         g1["stream_mb"] + g2["stream_mb"]]),
         "combine": np.array([1.0, 0.0 if stream else mb, mb if stream else 0.0, k * d / 1e3]),
     }
 
@@ -216,9 +266,14 @@ class CostModel:
     coef: Dict[str, List[float]]
 
     def predict(self, T: int, d_model: int, E: int, k: int, d_expert: int,
-                counts: Optional[Sequence[int]] = None) -> Dict[str, float]:
-        """Predicted phase times (us) and their sum ("step")."""
-        s = Sample(T, d_model, E, k, d_expert, list(counts) if counts is not None else balanced_counts(T, E, k))
+                counts: Sequence[int]) -> Dict[str, float]:
+        """Predicted phase times (us) and their sum ("step") for the per-expert
+        selection counts of the routing at hand (e.g. moe_permute's counts;
+        balanced_counts() only for a perfectly balanced router: a real
+        router's imbalance adds tiles)."""
+        if counts is None or len(counts) != E or sum(counts) != T * k:
+            raise ValueError("predict needs the E per-expert selection counts of the routing (summing to T * k)")
+        s = Sample(T, d_model, E, k, d_expert, [int(c) for c in counts])
         f = features(s)
         out = {p: float(f[p] @ np.asarray(self.coef[p])) for p in PHASES}
         out["step"] = sum(out[p] for p in PHASES)

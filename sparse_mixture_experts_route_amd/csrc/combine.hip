@@ -134,6 +134,14 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_f32_kernel(
 
 }  // namespace
 
+bool combine_streams(const moe_problem_t& p) {
+  if (p.dtype != MOE_DTYPE_BF16) return false;
+  bool nt = (double)p.T * p.k * p.d_model * 2 >= (double)kCombineStreamBytes;
+  const char* force = getenv("MOE_COMBINE_NT");
+  if (force && force[0]) nt = atoi(force) != 0;
+  return nt;
+}
+
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv, const float* gate,
                           void* y, hipStream_t s) {
   const int64_t rows = p.T * p.k;
@@ -149,10 +157,7 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int3
     // wide) combine in 49 instead of 58 us, 1.75 GB in 352 instead of 402 us;
     // at 32 MB (still in the last-level cache after the expert GEMM) plain
     // accesses are ~1 us faster. MOE_COMBINE_NT=0|1 forces the choice.
-    bool nt = (double)rows * p.d_model * 2 >= (double)kCombineStreamBytes;
-    const char* force = getenv("MOE_COMBINE_NT");
-    if (force && force[0]) nt = atoi(force) != 0;
-    if (nt)
+    if (combine_streams(p))
       hipLaunchKernelGGL(combine_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kCombineWaves * kWave), 0, s,
                          (const u32x4*)y_perm, inv, gate, (u32x4*)y, p.T, p.k, row_vecs, rows, chunks);
     else

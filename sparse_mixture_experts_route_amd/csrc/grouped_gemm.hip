@@ -964,24 +964,15 @@ void launch_kernel(unsigned grid, hipStream_t s, const void* A, const int32_t* o
 }
 
 template <int BM, int BN, int BK, int S, int OCC, int WM = 2, int WN = 2, bool FILL = false>
-hipError_t launch_bf16(const void* A, const int32_t* offsets, const void* B, void* C, float* partials,
-                       int32_t* counters, int64_t R, int K, int N, int E, bool gelu, const int32_t* perm,
-                       int64_t a_rows, hipStream_t s) {
-  const int n_tiles = (int)ceil_div(N, BN);
-  const int64_t tiles_ub = tiles_upper_bound(R, N, E, BM, BN);
-  if (tiles_ub > INT32_MAX || K % BK != 0) return hipErrorInvalidValue;
-  const int64_t grid = persistent_grid(tiles_ub, OCC, FILL);
-  const int nb = (int)(grid / 8);
-  const int nk = K / BK;
-  // MOE_GEMM_SPLIT_MIN_STEPS=<n> overrides the split threshold (0: split every small leftover)
-  int min_steps = kSplitMinSteps;
-  const char* ms = getenv("MOE_GEMM_SPLIT_MIN_STEPS");
-  if (ms && ms[0]) min_steps = max(0, atoi(ms));
-  // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
-  const int max_rem = FILL ? nb - 1 : nb / 3;
+hipError_t launch_bf16(const GemmGeom& geo, const void* A, const int32_t* offsets, const void* B, void* C,
+                       float* partials, int32_t* counters, int64_t R, int K, int N, int E, bool gelu,
+                       const int32_t* perm, int64_t a_rows, hipStream_t s) {
+  if (geo.bm != BM || geo.bn != BN || geo.bk != BK || tiles_upper_bound(R, N, E, BM, BN) > INT32_MAX || K % BK != 0)
+    return hipErrorInvalidValue;
+  const int n_tiles = geo.n_tiles, nb = geo.nb, nk = geo.nk, min_steps = geo.min_steps, max_rem = geo.max_rem;
+  const int64_t grid = geo.grid;
   const int gm = group_m();
-  // a block per CU slot (decode-sized batches): split tiles may be completed inside the launch
-  const bool ink = FILL && split_in_launch(R, E, gelu);
+  const bool ink = FILL && geo.in_launch;
   if (ink && (!counters || max_rem > kSplitCountersPerXcd)) return hipErrorInvalidValue;
   // fixup blocks: FS per split tile, each looping over up to kFixupRounds tiles
   constexpr int FS = fixup_sub<BM, BN>();
@@ -1089,6 +1080,46 @@ int pick_tile(int64_t R, int K, int N, int E) {
 
 }  // namespace
 
+GemmGeom gemm_geom(int64_t R, int K, int N, int E, bool gelu) {
+  GemmGeom g;
+  g.shape = pick_tile(R, K, N, E);
+  const TileShape& ts = kShapes[g.shape];
+  g.bm = ts.bm;
+  g.bn = ts.bn;
+  g.bk = ts.bk;
+  g.n_tiles = (int)ceil_div(N, ts.bn);
+  g.grid = (int)persistent_grid(tiles_upper_bound(R, N, E, ts.bm, ts.bn), ts.occ, ts.fill);
+  g.nb = g.grid / 8;
+  g.nk = K / ts.bk;
+  // MOE_GEMM_SPLIT_MIN_STEPS=<n> overrides the split threshold (0: split every small leftover)
+  g.min_steps = split_min_steps();
+  // split leftover tiles number at most max_rem per XCD, and none when K is short (split_leftover)
+  g.max_rem = ts.fill ? g.nb - 1 : g.nb / 3;
+  g.in_launch = ts.fill && split_in_launch(R, E, gelu);
+  return g;
+}
+
+void gemm_xcd_plan(const GemmGeom& g, const int32_t* counts, int E, GemmXcdPlan* out) {
+  int64_t total = 0;
+  for (int e = 0; e < E; ++e) total += counts[e] > 0 ? ceil_div((int64_t)counts[e], g.bm) * g.n_tiles : 0;
+  out->tiles = total;
+  out->full = out->rem = out->split = out->split_xcds = 0;
+  int64_t most = -1;
+  for (int x = 0; x < 8; ++x) {
+    // the same ranges and split rule as the kernels (contiguous eighths of the tile list)
+    const int64_t t = total * (x + 1) / 8 - total * x / 8;
+    const int full = (int)(t / g.nb), rem = (int)(t - (int64_t)full * g.nb);
+    const bool split = split_leftover(rem, g.nb, g.nk, g.min_steps, g.max_rem);
+    out->split_xcds += split ? 1 : 0;
+    if (t > most) {
+      most = t;
+      out->full = full;
+      out->rem = rem;
+      out->split = split ? 1 : 0;
+    }
+  }
+}
+
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E) {
   if (dtype != MOE_DTYPE_BF16) return 0;
   const TileShape& ts = kShapes[pick_tile(R, K, N, E)];
@@ -1118,30 +1149,31 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
                          offsets, (const float*)B, (float*)C, R, K, N, E, n_tiles, (int)grid_tiles);
     return hipGetLastError();
   }
-  switch (pick_tile(R, K, N, E)) {
+  const GemmGeom geo = gemm_geom(R, K, N, E, gelu);
+  switch (geo.shape) {
     case 0:
-      return launch_bf16<256, 256, 64, 2, 1>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<256, 256, 64, 2, 1>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                              a_rows, s);
     case 1:
-      return launch_bf16<256, 256, 32, 4, 1>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<256, 256, 32, 4, 1>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                              a_rows, s);
     case 2:
-      return launch_bf16<256, 128, 32, 3, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<256, 128, 32, 3, 2>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                              a_rows, s);
     case 3:
-      return launch_bf16<128, 128, 64, 2, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<128, 128, 64, 2, 2>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                              a_rows, s);
     case 4:
-      return launch_bf16<128, 128, 32, 4, 2>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<128, 128, 32, 4, 2>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                              a_rows, s);
     case 5:
-      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<256, 256, 64, 2, 1, 2, 4>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                                    a_rows, s);
     case kDecodeTile:
-      return launch_bf16<32, 256, 64, 4, 1, 1, 4, true>(A, offsets, B, C, partials, counters, R, K, N, E, gelu,
+      return launch_bf16<32, 256, 64, 4, 1, 1, 4, true>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu,
                                                         perm, a_rows, s);
     default:
-      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
+      return launch_bf16<256, 256, 32, 4, 1, 2, 4>(geo, A, offsets, B, C, partials, counters, R, K, N, E, gelu, perm,
                                                    a_rows, s);
   }
 }

@@ -51,6 +51,15 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
                                 int32_t* blockcounts, int32_t* blockbase, hipStream_t s, int32_t* zero = nullptr,
                                 int nzero = 0);
 
+// Form of launch_permute_index for p: 0 one workgroup (T <= kSmallPermuteT,
+// k <= 8), 1 per-block histograms then a scatter that scans for itself,
+// 2 histograms, a scan launch and the scatter.
+int permute_form(const moe_problem_t& p);
+// Whether launch_combine streams y_perm and y with non-temporal accesses.
+bool combine_streams(const moe_problem_t& p);
+// Tokens per router block (32 or 64).
+int route_rt(const moe_problem_t& p);
+
 // p[0 .. n) = 0 (one small block)
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 
@@ -74,6 +83,27 @@ hipError_t launch_grouped_gemm(int dtype, const void* A, const int32_t* offsets,
 constexpr int kSplitCountersPerXcd = 64;
 constexpr int kGemmSplitCounters = 8 * kSplitCountersPerXcd;
 bool grouped_gemm_uses_counters(int dtype, int64_t R, int K, int N, int E, bool gelu);
+
+// Launch geometry of a bf16 grouped GEMM as launch_grouped_gemm picks it
+// (host only): block tile (index into the tile table), persistent grid, K
+// steps per tile, split rule, and whether split tiles are completed inside the
+// launch (gelu: the launch's activation).
+struct GemmGeom {
+  int shape, bm, bn, bk;
+  int grid, nb, nk, n_tiles;
+  int max_rem, min_steps;
+  bool in_launch;
+};
+GemmGeom gemm_geom(int64_t R, int K, int N, int E, bool gelu);
+// The tile list the kernels derive on the device for per-expert row counts
+// (host copy): total tiles, the whole rounds and leftover tiles of the XCD
+// with the most tiles and whether its leftover is split by K steps, and the
+// number of XCDs whose leftover is split.
+struct GemmXcdPlan {
+  int64_t tiles;
+  int full, rem, split, split_xcds;
+};
+void gemm_xcd_plan(const GemmGeom& g, const int32_t* counts, int E, GemmXcdPlan* out);
 
 // Host-only bound of the partial-sum workspace one launch_grouped_gemm call may use.
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);

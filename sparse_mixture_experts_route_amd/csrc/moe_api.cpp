@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
 #include <mutex>
 
 #include "internal.h"
@@ -464,6 +465,55 @@ MOE_API moe_status_t moe_backward(const moe_problem_t* p, const void* x, const v
   if (e == hipSuccess && (dbias || load_frac || mean_prob))
     e = moe::launch_bwd_stats(*p, w.prob, w.dlogit, w.counts, w.stat_part, load_frac, mean_prob, dbias, s);
   return hip_status(e);
+}
+
+MOE_API moe_status_t moe_plan(const moe_problem_t* p, const int32_t* host_counts, moe_plan_t* plan) {
+  const moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (host_counts)
+    for (int e = 0; e < p->E; ++e)
+      if (host_counts[e] < 0) return MOE_ERR_INVALID_ARGUMENT;
+  moe_plan_t out;
+  memset(&out, 0, sizeof(out));
+  out.route_splits = moe::route_splits(*p);
+  out.route_tokens_per_block = moe::route_rt(*p);
+  out.route_fused_permute = moe::route_permute_fused(*p) ? 1 : 0;
+  out.permute_form = moe::permute_form(*p);
+  out.gather_in_gemm = gather_supported(*p) ? 1 : 0;
+  out.combine_streaming = moe::combine_streams(*p) ? 1 : 0;
+  const int64_t R = p->T * p->k;
+  for (int i = 0; i < 2; ++i) {
+    moe_gemm_plan_t& g = out.gemm[i];
+    if (p->dtype != MOE_DTYPE_BF16) {
+      memset(&g, 0xff, sizeof(g));  // every field -1: the float32 path has no persistent plan
+      continue;
+    }
+    const int K = i == 0 ? p->d_model : p->d_expert, N = i == 0 ? p->d_expert : p->d_model;
+    const moe::GemmGeom geo = moe::gemm_geom(R, K, N, p->E, i == 0);
+    g.tile = geo.shape;
+    g.bm = geo.bm;
+    g.bn = geo.bn;
+    g.bk = geo.bk;
+    g.grid = geo.grid;
+    g.k_steps = geo.nk;
+    g.max_split = geo.max_rem;
+    g.min_steps = geo.min_steps;
+    g.split_in_launch = geo.in_launch ? 1 : 0;
+    g.tiles = -1;
+    g.xcd_rounds = g.xcd_leftover = g.xcd_split = g.split_xcds = -1;
+    if (host_counts) {
+      moe::GemmXcdPlan xp;
+      moe::gemm_xcd_plan(geo, host_counts, p->E, &xp);
+      g.tiles = xp.tiles;
+      g.xcd_rounds = xp.full;
+      g.xcd_leftover = xp.rem;
+      g.xcd_split = xp.split;
+      g.split_xcds = xp.split_xcds;
+    }
+  }
+  *plan = out;
+  return MOE_OK;
 }
 
 // ---- the index permute without a workspace argument

@@ -384,12 +384,22 @@ bool route_permute_fused(const moe_problem_t& p) {
   return ns > 1 && p.T <= fused_route_tokens() && p.k <= 8 && (int64_t)ns * p.T * p.E * 4 <= 256 * 1024;
 }
 
+int permute_form(const moe_problem_t& p) {
+  if (p.T <= kSmallPermuteT && p.k <= 8) return 0;
+  // MOE_PERMUTE_FUSED_SCAN=0|1 forces the choice (1 only within kFusedScanBlocks)
+  bool fused = permute_blocks(p.T) <= kFusedScanBlocks;
+  const char* force = getenv("MOE_PERMUTE_FUSED_SCAN");
+  if (force && force[0]) fused = fused && atoi(force) != 0;
+  return fused ? 1 : 2;
+}
+
 hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* inv, int32_t* blockcounts, int32_t* blockbase,
                                 hipStream_t s, int32_t* zero, int nzero) {
   if (!zero) nzero = 0;
   if (nzero < 0 || nzero > kSmallThreads) return hipErrorInvalidValue;
-  if (p.T <= kSmallPermuteT && p.k <= 8) {
+  const int form = permute_form(p);
+  if (form == 0) {
     hipLaunchKernelGGL(permute_small_kernel<false>, dim3(1), dim3(kSmallThreads), 0, s, idx, nullptr, 0, nullptr,
                        nullptr, nullptr, (int)p.T, p.k, p.E, counts, offsets, perm, inv, zero, nzero);
     return hipGetLastError();
@@ -399,11 +409,7 @@ hipError_t launch_permute_index(const moe_problem_t& p, const int32_t* idx, int3
                      nzero);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // MOE_PERMUTE_FUSED_SCAN=0|1 forces the choice (1 only within kFusedScanBlocks)
-  bool fused = nb <= kFusedScanBlocks;
-  const char* force = getenv("MOE_PERMUTE_FUSED_SCAN");
-  if (force && force[0]) fused = fused && atoi(force) != 0;
-  if (fused) {
+  if (form == 1) {
     hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)nb), dim3(kTB), 0, s, idx, p.T, p.k, p.E, blockcounts,
                        nb, counts, offsets, perm, inv);
     return hipGetLastError();

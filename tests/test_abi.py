@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         "moe_workspace_size", "moe_route", "moe_route_ws", "moe_permute", "moe_permute_index",
         "moe_permute_index_noalloc", "moe_grouped_ffn",
         "moe_grouped_ffn_gather", "moe_combine", "moe_forward", "moe_forward_train", "moe_backward",
-        "moe_status_str"])
+        "moe_status_str", "moe_plan"])
 
 
 def test_library_exports_every_declared_symbol(libmoe_path):
@@ -176,3 +176,20 @@ def test_permute_index_noalloc_rejects_before_launch(moe, lib):
     T_max = slots // 256 * 256  # ceil(T / 256) * 256 experts == slots
     big = P(moe, T=T_max + 1, d=128, E=256, k=2, de=256)
     assert lib.moe_permute_index_noalloc(ctypes.byref(big), A, A, A, A, A, s) == WS_SMALL
+
+
+def test_plan_is_host_only_and_checks_its_arguments(moe, lib):
+    """moe_plan answers on the host (no GPU here) and rejects bad problems,
+    a NULL plan and negative counts."""
+    p = P(moe, T=4096, d=2048, E=8, k=2, de=8192)
+    out = moe.moe_plan(p, [1024] * 8)
+    assert out["gemm"][0]["tiles"] == 8 * 4 * 32 and out["gemm"][1]["tiles"] == 8 * 4 * 8
+    assert moe.moe_plan(p)["gemm"][0]["tiles"] == -1
+    assert lib.moe_plan(ctypes.byref(p), None, None) == INVALID
+    bad = (ctypes.c_int32 * 8)(*([1024] * 7 + [-1]))
+    from sparse_mixture_experts_route_amd._lib import Plan
+    plan = Plan()
+    assert lib.moe_plan(ctypes.byref(p), ctypes.cast(bad, ctypes.c_void_p), ctypes.byref(plan)) == INVALID
+    assert lib.moe_plan(ctypes.byref(P(moe, E=0)), None, ctypes.byref(plan)) == INVALID
+    f32 = moe.moe_plan(P(moe, dtype=0))
+    assert all(v == -1 for v in f32["gemm"][0].values())

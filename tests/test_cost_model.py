@@ -9,6 +9,7 @@ MFU (the yardstick of the MOSAIC summary's operator-level performance model,
 "Compute-Optimal Is Not Cluster-Optimal", method item 2).
 """
 
+import numpy as np
 import pytest
 
 from sparse_mixture_experts_route_amd import cost_model as cm
@@ -46,7 +47,58 @@ def test_tile_choice_and_split_rule():
 
 def test_prediction_scales_with_work():
     m = cm.calibrated()
-    a = m.predict(4096, 2048, 8, 2, 8192)
-    b = m.predict(8192, 2048, 8, 2, 8192)
+    a = m.predict(4096, 2048, 8, 2, 8192, cm.balanced_counts(4096, 8, 2))
+    b = m.predict(8192, 2048, 8, 2, 8192, cm.balanced_counts(8192, 8, 2))
     assert b["ffn"] > 1.6 * a["ffn"] and b["step"] > a["step"]
     assert set(a) == set(cm.PHASES) | {"step"}
+
+
+def _routed_counts(T, E, k, seed, skew):
+    """Per-expert selection counts of k distinct experts per token drawn with
+    Gumbel top-k from expert weights exp(skew * N(0, 1)) (skew 0: uniform)."""
+    rng = np.random.default_rng(seed)
+    logp = skew * rng.standard_normal(E)
+    counts = np.zeros(E, dtype=np.int64)
+    for t0 in range(0, T, 4096):
+        n = min(4096, T - t0)
+        g = logp[None, :] + rng.gumbel(size=(n, E))
+        top = np.argpartition(-g, k - 1, axis=1)[:, :k]
+        counts += np.bincount(top.ravel(), minlength=E)
+    assert counts.sum() == T * k and counts.max() <= T
+    return [int(c) for c in counts]
+
+
+PLAN_SHAPES = cm.FIT_SHAPES + cm.HELD_OUT_SHAPES + [
+    (3, 1024, 5, 2, 512), (17, 2048, 64, 8, 1024), (40, 2048, 8, 2, 8192), (320, 2048, 8, 2, 8192),
+    (1025, 1024, 256, 1, 256), (16385, 2048, 64, 8, 1024), (70000, 512, 32, 4, 1536), (2500, 4096, 100, 6, 704),
+]
+
+
+def test_plan_matches_the_library():
+    """The model's restatement of the launcher's choices (router split and
+    block, permute form, combine mode, each GEMM's tile, grid, split rule and
+    tile list for routed counts) equals what the library itself reports
+    through moe_plan, for the calibration shapes and others, with balanced,
+    uniform-random and skewed routings."""
+    import os
+    from sparse_mixture_experts_route_amd import make_problem, moe_plan
+    forced = [v for v in os.environ if v.startswith("MOE_")]
+    assert not forced, f"launcher overrides set: {forced}"
+    checked = 0
+    for i, (T, d, E, k, de) in enumerate(PLAN_SHAPES):
+        p = make_problem(T, d, E, k, de, "bf16")
+        assert cm.plan(T, d, E, k, de) == moe_plan(p), (T, d, E, k, de)
+        for j, counts in enumerate([cm.balanced_counts(T, E, k), _routed_counts(T, E, k, i, 0.0),
+                                    _routed_counts(T, E, k, i, 1.5)]):
+            mine, lib = cm.plan(T, d, E, k, de, counts), moe_plan(p, counts)
+            assert mine == lib, (T, d, E, k, de, j, mine, lib)
+            checked += 1
+    assert checked == 3 * len(PLAN_SHAPES)
+
+
+def test_predict_needs_routed_counts():
+    m = cm.calibrated()
+    with pytest.raises(ValueError):
+        m.predict(4096, 2048, 8, 2, 8192, None)
+    with pytest.raises(ValueError):
+        m.predict(4096, 2048, 8, 2, 8192, [1] * 8)
