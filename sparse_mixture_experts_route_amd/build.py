@@ -48,23 +48,36 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source for gfx950 and link libmoe.so next to this file. Always rebuilds."""
+# AddressSanitizer on the host code only (argument checks, workspace layout,
+# launch planning); the device code is built as usual
+HOST_ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, jobs: int = 8, host_asan_dir: str = "") -> str:
+    """Compile every source for gfx950 and link libmoe.so next to this file. Always rebuilds.
+
+    With host_asan_dir, build a copy whose host code carries AddressSanitizer
+    instead, as host_asan_dir/libmoe_asan.so (a process loading it needs the
+    ASan runtime preloaded); libmoe.so is left as it is."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = host_asan_dir or BUILD_DIR
+    out = os.path.join(bdir, "libmoe_asan.so") if host_asan_dir else LIB_PATH
+    extra = HOST_ASAN_FLAGS if host_asan_dir else []
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *compile_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+    tmp = out + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libsan"] if host_asan_dir else []
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *link_extra,
           "-Wl,-rpath,/opt/rocm/lib"], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
