@@ -44,7 +44,11 @@
 //     host synchronisation on the routing is needed;
 //   * a small last round of long tiles is split over all of the XCD's blocks
 //     by K steps (stream-K style): float32 partial sums go to a workspace and
-//     gemm_fixup_kernel adds them in K order (deterministic) and stores.
+//     gemm_fixup_kernel adds them in K order (deterministic) and stores. The
+//     32-row weight-streaming tile of decode-sized batches may instead finish
+//     them inside its own launch (INK): the last block to store a tile's
+//     partial sums, found with a per-tile counter, adds them in the same
+//     order, so the bits are the same either way.
 // float32 path: a plain LDS-tiled FMA kernel (the fp32 workload is small).
 #include <stdlib.h>
 #include <string.h>
