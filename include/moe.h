@@ -117,6 +117,8 @@ typedef struct {
   int32_t combine_streaming;      /* 1: y_perm and y streamed with non-temporal accesses */
   moe_gemm_plan_t gemm[2];        /* first (x W1, GELU) and second (H W2) grouped GEMM;
                                      every field -1 for float32 problems */
+  int32_t forward_one_launch;     /* 1: moe_forward runs the whole (small float32) layer as one
+                                     launch, one workgroup per token */
 } moe_plan_t;
 
 moe_status_t moe_plan(const moe_problem_t* p, const int32_t* host_counts, moe_plan_t* plan);

@@ -15,7 +15,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "grouped_gemm_bwd.hip", "backward.hip",
-           "moe_api.cpp"]
+           "small_layer.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -232,6 +232,7 @@ def plan(T: int, d_model: int, E: int, k: int, d_expert: int, counts: Optional[S
             for key in ("tiles", "xcd_rounds", "xcd_leftover", "xcd_split", "split_xcds"):
                 g[key] = -1
     out["gemm"] = gemms
+    out["forward_one_launch"] = 0  # the one-launch layer is float32 only
     return out
 
 

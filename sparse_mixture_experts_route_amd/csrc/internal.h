@@ -108,6 +108,12 @@ void gemm_xcd_plan(const GemmGeom& g, const int32_t* counts, int E, GemmXcdPlan*
 // Host-only bound of the partial-sum workspace one launch_grouped_gemm call may use.
 size_t grouped_gemm_partials_bytes(int dtype, int64_t R, int K, int N, int E);
 
+// The whole layer of a small float32 problem in one launch (small_layer.hip):
+// the same y, bit for bit, as route -> permute -> grouped FFN -> combine.
+bool small_layer_fused(const moe_problem_t& p);
+hipError_t launch_small_layer(const moe_problem_t& p, const void* x, const void* w_router, const float* bias,
+                              const void* W1, const void* W2, void* y, hipStream_t s);
+
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* inv,
                           const float* gate, void* y, hipStream_t s);
 

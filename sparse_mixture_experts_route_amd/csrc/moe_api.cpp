@@ -339,9 +339,12 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const void* x, const vo
       !aligned16(ws) || (router_bias && !aligned16(router_bias)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < stage_bytes(*p, MOE_STAGE_FORWARD)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  // a small float32 layer: one launch, one workgroup per token
+  if (moe::small_layer_fused(*p))
+    return hip_status(moe::launch_small_layer(*p, x, w_router, router_bias, W1, W2, y, s));
   Carver c(align_ws(ws));
   const ForwardWs w = carve_forward(c, *p);
-  hipStream_t s = (hipStream_t)stream;
   const int64_t R = p->T * p->k;
   hipError_t e;
   if (moe::route_permute_fused(*p)) {
@@ -482,6 +485,7 @@ MOE_API moe_status_t moe_plan(const moe_problem_t* p, const int32_t* host_counts
   out.permute_form = moe::permute_form(*p);
   out.gather_in_gemm = gather_supported(*p) ? 1 : 0;
   out.combine_streaming = moe::combine_streams(*p) ? 1 : 0;
+  out.forward_one_launch = moe::small_layer_fused(*p) ? 1 : 0;
   const int64_t R = p->T * p->k;
   for (int i = 0; i < 2; ++i) {
     moe_gemm_plan_t& g = out.gemm[i];

@@ -28,6 +28,7 @@
 #include "gemm_lanes.h"
 #include "internal.h"
 #include "lds_dma.h"
+#include "route_fma.h"
 #include "topk.h"
 
 namespace moe {
@@ -256,76 +257,15 @@ __global__ __launch_bounds__(kFinalizeWaves * kWave) void route_finalize_kernel(
 constexpr int kRouteWaves = 4;  // tokens per block
 
 template <typename Tin>
-struct Vec;
-template <>
-struct Vec<bf16_bits> {
-  static constexpr int N = 8;  // elements per 16-byte piece
-  __device__ static void load(const bf16_bits* p, float* f) {
-    const u32x4 v = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
-      f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
-    }
-  }
-};
-template <>
-struct Vec<float> {
-  static constexpr int N = 4;
-  __device__ static void load(const float* p, float* f) {
-    const f32x4 v = *(const f32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = v[i];
-  }
-};
-
-template <typename Tin>
-__device__ __forceinline__ float load_one(const Tin* p);
-template <>
-__device__ __forceinline__ float load_one<float>(const float* p) { return *p; }
-template <>
-__device__ __forceinline__ float load_one<bf16_bits>(const bf16_bits* p) { return bf16_to_f32(*p); }
-
-template <typename Tin>
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_fma_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate, int64_t T, int d, int E,
     int k) {
-  constexpr int VN = Vec<Tin>::N;
   __shared__ float lg[kRouteWaves][256];
   const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kRouteWaves + wave;
   const bool valid = t < T;
-  const Tin* xr = x + (valid ? t : 0) * (int64_t)d;
-
-  for (int e0 = 0; e0 < E; e0 += 8) {
-    const int ne = min(8, E - e0);
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    if (valid) {
-      // lane takes 16-byte pieces c0 = lane*VN, lane*VN + 64*VN, ...
-      for (int c0 = lane * VN; c0 < d; c0 += kWave * VN) {
-        float xv[VN];
-        Vec<Tin>::load(xr + c0, xv);
-#pragma unroll
-        for (int i = 0; i < VN; ++i) {
-          const Tin* w = wr + (int64_t)(c0 + i) * E + e0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (q < ne) acc[q] = fmaf(xv[i], load_one(w + q), acc[q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = wave_sum(acc[q]);
-    if (lane == 0) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (q < ne) lg[wave][e0 + q] = acc[q] + (bias ? bias[e0 + q] : 0.0f);
-    }
-  }
+  route_row_fma(x + (valid ? t : 0) * (int64_t)d, wr, bias, d, E, valid, lg[wave]);
   __syncthreads();
   if (valid) select_topk(lg[wave], E, k, t, logits, idx, gate);
 }

@@ -33,7 +33,7 @@ class GemmPlan(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("route_splits", "route_tokens_per_block", "route_fused_permute",
                                               "permute_form", "gather_in_gemm", "combine_streaming")] + \
-               [("gemm", GemmPlan * 2)]
+               [("gemm", GemmPlan * 2), ("forward_one_launch", ctypes.c_int32)]
 
 
 def main(path, short_counts=False):
